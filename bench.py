@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark of the layer-wise mixed-precision KV cache on one MI355X.
+
+One step = one decode token for every request, through every layer: append the
+token's fp16 K/V (tail write, and the 32-token group quantize-and-pack when the
+tail fills), then split-KV decode attention over the packed cache and the
+log-sum-exp merge. Inputs are seeded synthetic tensors (synthetic/), resident in
+HBM before the timed region. Each step is replayed from a HIP graph captured
+once per step position of the decode cycle.
+
+Prints one JSON line (the benchmark contract), with a roofline object for the
+split pass (algorithmic bytes per launch over its HIP-event duration) and a
+CPU baseline (the oracle, timed on a bounded sample of the same step).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synthetic as syn  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode-attention tokens/s and effective HBM GB/s (% of peak), batch 64, 1 GPU"
+
+
+# ----------------------------------------------------------------- workloads
+def _llama_mixed_map(seed):
+    hi = set(syn.seeded_choice(seed, syn.T_MAP, 32, 8))
+    return [(4, 4) if l in hi else (4, 2) for l in range(32)]
+
+
+def _qwen_map(seed):
+    hi = set(syn.seeded_choice(seed, syn.T_MAP, 28, 9, salt=1))
+    return [(8, 4) if l in hi else (4, 2) for l in range(28)]
+
+
+# prefill P tokens; a timed step appends token P + (i mod cycle), so the cache
+# holds P + 1 .. P + cycle tokens over a cycle.
+WORKLOADS = {
+    "single-head-k8v4-l512": dict(layers=1, hq=1, hkv=1, batch=1, prefill=511, cycle=1,
+                                  map=lambda s: [(8, 4)], outliers=(4, 10.0),
+                                  desc="1 layer, 1 request, 1 q/KV head, 512 cached tokens, K8V4"),
+    "llama31-8b-b64-kivi8-trace": dict(layers=32, hq=32, hkv=8, batch=64, prefill=128, cycle=128,
+                                       map=lambda s: [(8, 8)] * 32, outliers=(4, 10.0),
+                                       desc="Llama-3.1-8B attention shape, batch 64, 128-token prompt + "
+                                            "128 decode steps, uniform K8V8"),
+    "llama31-8b-b64-mixed325-l2048": dict(layers=32, hq=32, hkv=8, batch=64, prefill=2047, cycle=32,
+                                          map=_llama_mixed_map, outliers=(4, 10.0),
+                                          desc="Llama-3.1-8B shape, batch 64, context 2048..2079, seeded "
+                                               "24 x K4V2 + 8 x K4V4 (3.25 bits)"),
+    "qwen25-7b-b32-map396-l8192": dict(layers=28, hq=28, hkv=4, batch=32, prefill=8191, cycle=32,
+                                       map=_qwen_map, outliers=(8, 20.0),
+                                       desc="Qwen2.5-7B shape, batch 32, context 8192..8223, seeded "
+                                            "9 x K8V4 + 19 x K4V2 (3.96 bits)"),
+}
+DEFAULT_WORKLOAD = "llama31-8b-b64-kivi8-trace"
+
+
+def capacity(w):
+    return w["prefill"] + w["cycle"]
+
+
+class Workload:
+    """A planned, prefilled cache on the GPU plus the inputs of every decode step."""
+
+    def __init__(self, name, seed=0, device="cuda", num_splits=0, gen_chunk=8):
+        import torch
+
+        import layer_wise_mixed_amd as kvq
+
+        self.name, self.seed, self.kvq = name, seed, kvq
+        w = self.w = WORKLOADS[name]
+        self.L, self.B, self.Hq, self.Hkv = w["layers"], w["batch"], w["hq"], w["hkv"]
+        self.P, self.C = w["prefill"], w["cycle"]
+        self.cap = capacity(w)
+        self.cfg = w["map"](seed)
+        self.outliers = w["outliers"]
+        self.shape = kvq.make_shape(self.Hq, self.Hkv, self.B, max_tokens=self.cap)
+        self.plan = kvq.plan_layers(self.shape, self.cfg)
+        self.cache = torch.empty(self.plan.total_bytes, dtype=torch.uint8, device=device)
+        self.scale = 1.0 / math.sqrt(128.0)
+        self.num_splits = num_splits
+        zeros = torch.zeros(self.B, dtype=torch.int32, device=device)
+        for l in range(self.L):  # prefill, a few requests at a time
+            for r0 in range(0, self.B, gen_chunk):
+                rs = range(r0, min(self.B, r0 + gen_chunk))
+                k = self.keys(l, rs, 0, self.P, device)
+                v = syn.values_fp16(seed, l, rs, range(self.Hkv), 0, self.P, device=device)
+                off = r0 * self.Hkv * self.plan.layers[l].stream_bytes
+                kvq.quantize_append(self.plan, l, self.cache[off:], k, v, zeros[: len(rs)])
+                del k, v
+        torch.cuda.synchronize()
+        # decode-step inputs: [cycle][batch][heads][1][128] and q [cycle][batch][Hq][128]
+        self.k_dec, self.v_dec, self.q = [], [], []
+        for l in range(self.L):
+            k = self.keys(l, range(self.B), self.P, self.C, device)
+            v = syn.values_fp16(seed, l, range(self.B), range(self.Hkv), self.P, self.C, device=device)
+            self.k_dec.append(k.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
+            self.v_dec.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
+            qq = syn.queries_steps_fp16(seed, l, self.B, self.Hq, 0, self.C, device=device)
+            self.q.append(qq.permute(2, 0, 1, 3).contiguous())
+        self.lens_base = torch.full((self.B,), self.P, dtype=torch.int32, device=device)
+        self.lens_before = self.lens_base.clone()
+        self.lens_after = self.lens_base + 1
+        self.max_len = self.cap
+        self.splits = num_splits or kvq.num_splits(self.plan, 0, self.B, self.max_len)
+        ws = kvq.workspace_bytes(self.plan, self.B, self.max_len, self.splits)
+        self.ws = torch.empty(ws // 4 + 1, dtype=torch.float32, device=device)
+        self.out = torch.empty(self.B, self.Hq, 128, dtype=torch.float16, device=device)
+        torch.cuda.synchronize()
+
+    def keys(self, layer, requests, t0, n, device):
+        cnt, fac = self.outliers
+        return syn.keys_fp16(self.seed, layer, requests, range(self.Hkv), t0, n, outlier_count=cnt,
+                             outlier_factor=fac, num_kv_heads=self.Hkv, device=device)
+
+    def reset(self):
+        self.lens_before.copy_(self.lens_base)
+        self.lens_after.copy_(self.lens_base)
+        self.lens_after.add_(1)
+
+    def step(self, i):
+        """Launch one decode step (all layers) for cycle position i."""
+        kvq = self.kvq
+        for l in range(self.L):
+            kvq.quantize_append(self.plan, l, self.cache, self.k_dec[l][i], self.v_dec[l][i], self.lens_before)
+            kvq.decode_attention(self.plan, l, self.cache, self.q[l][i], self.lens_after, self.max_len, self.scale,
+                                 self.out, None, self.ws, self.splits)
+        self.lens_before.add_(1)
+        self.lens_after.add_(1)
+
+    def split_bytes(self, i):
+        """Algorithmic bytes the split passes of step i read: packed codes + scale/zero of the
+        full groups, the fp16 tail, and q."""
+        L = self.P + i + 1
+        lq, t = (L // 32) * 32, L % 32
+        total = 0
+        for l in range(self.L):
+            rb = self.plan.layers[l].record_bytes
+            total += self.B * self.Hkv * ((lq // 32) * rb + t * 512) + self.B * self.Hq * 256
+        return total
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "layer_wise_mixed_amd", "csrc"))):
+        with open(os.path.join(ROOT, "layer_wise_mixed_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload, achieved_bytes_per_launch):
+    """HBM bytes per split launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "split_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        e = d.get(workload)
+        if not e or e.get("source_hash") != _source_hash():
+            return None
+        return e["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+# -------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, max_seconds=20.0):
+    """The oracle, timed on host cores on a sample of the last decode step of the cycle:
+    unpack + dequantize its own packed streams, then fp64 attention."""
+    import numpy as np
+
+    import oracle
+
+    L = wl.P + wl.C  # the last step of the cycle
+    G = wl.Hq // wl.Hkv
+    layer = 0
+    lp = wl.plan.layers[layer]
+    kb, vb, kt = lp.k_bits, lp.v_bits, lp.k_axis == 1
+    cap_groups = wl.cap // 32
+    stride = oracle.stream_bytes(kb, vb, cap_groups)
+    # build the oracle's own packed cache for a sample of streams (not timed)
+    n_streams = min(wl.B * wl.Hkv, 64)
+    buf = np.zeros(n_streams * stride, np.uint8)
+    qs = np.zeros((n_streams, G, 128), np.float16)
+    cnt, fac = wl.outliers
+    for s in range(n_streams):
+        r, h = divmod(s, wl.Hkv)
+        k = syn.keys_fp16(wl.seed, layer, [r], [h], 0, L, outlier_count=cnt, outlier_factor=fac,
+                          num_kv_heads=wl.Hkv)[0, 0].numpy()
+        v = syn.values_fp16(wl.seed, layer, [r], [h], 0, L)[0, 0].numpy()
+        sq = oracle.quantize_stream(k, v, kb, vb, kt)
+        b, _ = oracle.pack_stream(sq, cap_groups)
+        buf[s * stride:(s + 1) * stride] = b
+        qs[s] = syn.queries_fp16(wl.seed, layer, wl.C - 1, r + 1, wl.Hq)[r, h * G:(h + 1) * G].numpy()
+    ids = np.arange(n_streams, dtype=np.int64)
+    lens = np.full(n_streams, L, np.int64)
+    threads = min(os.cpu_count() or 1, 16)
+    # repeat the sample until about max_seconds of wall time
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        _, _, used = oracle.decode_packed(buf, stride, ids, lens, kb, vb, kt, cap_groups, qs, G, wl.scale, threads)
+        reps += 1
+        if time.perf_counter() - t0 > max_seconds or reps >= 1000:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    per_stream = dt / n_streams
+    t_step = per_stream * wl.B * wl.Hkv * wl.L
+    return {"value": wl.B / t_step, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{n_streams} (request, KV head) streams of layer 0 at L={L}, repeated {reps}x "
+                      f"({dt * 1e3:.1f} ms each); step time scaled to {wl.B * wl.Hkv} streams x {wl.L} layers"}
+
+
+# ---------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: one decode cycle)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU leg (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import layer_wise_mixed_amd as kvq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kvq.load()
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    wl = Workload(args.workload, seed=args.seed, num_splits=args.splits)
+    K = args.steps if args.steps is not None else wl.C
+    W = args.warmup if args.warmup is not None else min(wl.C, 16)
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s: {wl.w['desc']}, splits={wl.splits}", file=sys.stderr,
+          flush=True)
+
+    stream = torch.cuda.Stream()
+    graphs = None
+    with torch.cuda.stream(stream):
+        wl.reset()
+        torch.cuda.synchronize()
+        n_pos = min(wl.C, max(K, W, 1))
+        kvq.timer_start(max(1, n_pos * wl.L))
+        if not args.no_graph:
+            # capture one graph per cycle position; capture itself runs nothing
+            graphs = []
+            for i in range(n_pos):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    wl.step(i)
+                graphs.append(g)
+            wl.reset()
+        torch.cuda.synchronize()
+
+        def run(i):
+            pos = i % wl.C
+            if pos == 0 and i > 0:
+                wl.reset()
+            if graphs is not None:
+                graphs[pos].replay()
+            else:
+                wl.step(pos)
+
+        if args.no_graph:
+            kvq.timer_stop()
+        for i in range(W):
+            run(i)
+        wl.reset()
+        if args.no_graph:
+            kvq.timer_start(max(1, K * wl.L))
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(K):
+            run(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = ev0.elapsed_time(ev1)
+        split_ms, split_n = kvq.timer_read(kvq.TIMER_SPLIT)
+        merge_ms, merge_n = kvq.timer_read(kvq.TIMER_MERGE)
+        app_ms, app_n = kvq.timer_read(kvq.TIMER_APPEND)
+        kvq.timer_stop()
+
+    ms_per_step = gpu_ms / K
+    tokens = wl.B * K
+    value = tokens / (gpu_ms / 1e3)
+    positions = [i % wl.C for i in range(K)]
+    bytes_total = sum(wl.split_bytes(p) for p in positions)
+    # timer slots hold the latest replay of each captured (position, layer) launch
+    if graphs is not None:
+        timed_pos = sorted(set(positions))
+        bytes_launches = sum(wl.split_bytes(p) for p in timed_pos)
+        n_launch = len(timed_pos) * wl.L
+    else:
+        bytes_launches = bytes_total
+        n_launch = K * wl.L
+    avg_split_s = (split_ms / 1e3) / max(split_n, 1)
+    achieved = (bytes_launches / n_launch) / avg_split_s / 1e9 if split_n else None
+    eff_gbs = bytes_total / (gpu_ms / 1e3) / 1e9
+    traffic = _traffic(args.workload, bytes_launches / max(n_launch, 1))
+    print(f"# {K} steps in {gpu_ms:.3f} ms GPU ({wall * 1e3:.1f} ms wall); split {split_n} launches avg "
+          f"{avg_split_s * 1e6:.2f} us; merge avg {merge_ms / max(merge_n, 1) * 1e3:.2f} us; append avg "
+          f"{app_ms / max(app_n, 1) * 1e3:.2f} us; whole-step effective {eff_gbs:.0f} GB/s", file=sys.stderr,
+          flush=True)
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "description": wl.w["desc"], "layers": wl.L, "batch": wl.B,
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": 128, "context": [wl.P + 1, wl.P + wl.C],
+                   "equiv_bits": wl.plan.equiv_bits, "splits": wl.splits,
+                   "launch": "eager" if graphs is None else "hip-graph per step",
+                   "effective_GBps_whole_step": eff_gbs, "effective_frac_whole_step": eff_gbs / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": traffic,
+                     "kernel": "decode split pass", "avg_launch_us": avg_split_s * 1e6,
+                     "bytes_per_launch": bytes_launches / max(n_launch, 1)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

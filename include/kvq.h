@@ -1,0 +1,238 @@
+/*
+ * kvq.h -- C ABI of the layer-wise mixed-precision KV-cache library for
+ * MI355X (gfx950).
+ *
+ * The library keeps a decode KV cache quantized at a static per-layer
+ * (key bits, value bits) pair chosen offline -- K8V4, K4V2, K8V8 and the
+ * like -- and runs split-KV decode attention straight from the packed
+ * codes. Sources of each operation are named on its declaration; the pages
+ * cited are: the KVTuner summary page (scime atlas), the "Mixed-precision
+ * KV-cache quantization per-layer sensitivity" notes page, the TriAxialKV
+ * notes page and the KVSplit Show HN thread.
+ *
+ * Conventions
+ *  - All device buffers (cache, inputs, outputs, workspace, page tables) are
+ *    owned by the caller. The library never allocates device memory and keeps
+ *    no state between calls except the optional timer below.
+ *  - Every call checks its host-side arguments first and returns a status
+ *    (KVQ_OK = 0, negative on error; kvq_last_error() gives a message, per
+ *    thread). Nothing throws or aborts across the ABI. Kernels run
+ *    asynchronously on the given stream (a hipStream_t; NULL = the null
+ *    stream).
+ *  - Values that live on the device (sequence lengths, page ids) are trusted
+ *    as far as the cache contents go; kernels never write outside the cache
+ *    region of the layer they were given.
+ *  - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *  - head_dim is 128 and the quantization group is 32 (elements of a group:
+ *    32 tokens of one channel for per-channel keys, 32 channels of one token
+ *    otherwise).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_MAX_LAYERS 256
+#define KVQ_HEAD_DIM 128
+#define KVQ_GROUP 32
+
+/* status codes */
+#define KVQ_OK 0
+#define KVQ_ERR_INVALID_ARG (-1) /* a null pointer, a size out of range, a bad layer index */
+#define KVQ_ERR_UNSUPPORTED (-2) /* a bit-width, axis or shape the library does not implement */
+#define KVQ_ERR_CAPACITY (-3)    /* the request would exceed the planned cache capacity */
+#define KVQ_ERR_WORKSPACE (-4)   /* the workspace is too small */
+#define KVQ_ERR_HIP (-5)         /* a HIP runtime call failed (message has the HIP error) */
+
+/* quantization axis */
+#define KVQ_AXIS_CHANNEL 0 /* one scale/zero per channel per 32-token group (keys) */
+#define KVQ_AXIS_TOKEN 1   /* one scale/zero per token per 32-channel group */
+
+/* output dtypes */
+#define KVQ_OUT_F16 0
+#define KVQ_OUT_F32 1
+
+typedef void *kvq_stream_t; /* a hipStream_t */
+
+/* Cache geometry shared by all layers. */
+typedef struct kvq_shape {
+    int32_t num_q_heads;  /* Hq */
+    int32_t num_kv_heads; /* Hkv; Hq must be a multiple, G = Hq / Hkv <= 16 */
+    int32_t head_dim;     /* must be 128 */
+    int32_t group_size;   /* must be 32 */
+    int32_t max_batch;    /* requests the cache holds */
+    int32_t max_tokens;   /* contiguous mode: token capacity of each request */
+    int32_t page_tokens;  /* 0 = contiguous streams; 16 = paged INT2/INT4 pool */
+    int32_t int2_pages;   /* paged: pages in the INT2 region (even) */
+    int32_t int4_pages;   /* paged: pages in the INT4 region */
+    int32_t reserved;
+} kvq_shape;
+
+/* One entry of the static per-layer map. Bits are 2, 4, 8 or 16 (16 = fp16
+ * passthrough, i.e. a layer left unquantized). v_axis must be
+ * KVQ_AXIS_TOKEN. */
+typedef struct kvq_layer_cfg {
+    int32_t k_bits;
+    int32_t v_bits;
+    int32_t k_axis;
+    int32_t v_axis;
+} kvq_layer_cfg;
+
+/* Byte geometry of one layer, filled by kvq_plan_layers. */
+typedef struct kvq_layer_plan {
+    int32_t k_bits, v_bits, k_axis, v_axis;
+    uint64_t offset;          /* start of the layer region in the cache buffer */
+    uint64_t bytes;           /* size of the layer region */
+    uint64_t record_bytes;    /* one 32-token group record */
+    uint64_t groups_cap;      /* contiguous: records per stream */
+    uint64_t stream_bytes;    /* contiguous: bytes per (request, KV head) stream */
+    uint64_t tail_offset;     /* contiguous: tail record inside a stream */
+    uint64_t int4_offset;     /* paged: start of the INT4 region (the pool split) */
+    uint64_t int2_page_bytes; /* paged: one INT2 page, all KV heads */
+    uint64_t int4_page_bytes; /* paged: one INT4 page, all KV heads */
+} kvq_layer_plan;
+
+/* Caller-owned, plain-old-data plan. */
+typedef struct kvq_plan {
+    kvq_shape shape;
+    int32_t num_layers;
+    int32_t reserved;
+    uint64_t total_bytes; /* device bytes the cache buffer must have */
+    double equiv_bits;    /* mean over layers of (k_bits + v_bits) / 2 */
+    double int2_fraction; /* paged: int2_pages / (int2_pages + int4_pages) */
+    kvq_layer_plan layers[KVQ_MAX_LAYERS];
+} kvq_plan;
+
+/* Paged-pool bookkeeping (device arrays, caller-owned). One page table per
+ * request, shared by all layers; its first int2_len/16 entries are INT2
+ * pages (aligned pairs 2k, 2k+1), the next ceil(int4_len/16) are INT4
+ * pages. Page ids below shape.int2_pages index the INT2 region, the others
+ * the INT4 region. */
+typedef struct kvq_pages {
+    const int32_t *page_table; /* [batch][max_pages_per_req] */
+    int32_t max_pages_per_req;
+    int32_t reserved;
+    const int32_t *int2_len; /* [batch] tokens in INT2 page pairs, a multiple of 32 */
+    const int32_t *int4_len; /* [batch] tokens in INT4 pages */
+    const int32_t *int2_add; /* append only, nullable: [batch] how many of the new tokens
+                                (the first ones, a multiple of 32) go to INT2 pages */
+} kvq_pages;
+
+/*
+ * kvq_plan_layers -- turn the static per-layer (bK, bV) map into byte
+ * offsets. Host only, pure, no HIP call.
+ * The map is searched offline and applied as is, with no decision at run
+ * time (notes page, "Facts": KVTuner's per-layer configuration is applied at
+ * inference with no online decision overhead; KVTuner summary page,
+ * "Approach"). Key and value bits are set separately (KVSplit thread:
+ * separate key and value flags). A layer may be left at 16 bits, the way
+ * vLLM excludes layers from KV quantization (notes page, "Facts").
+ * Paged mode (shape.page_tokens = 16) needs every layer at
+ * {2, 2, KVQ_AXIS_CHANNEL, KVQ_AXIS_TOKEN}: INT2 per-channel keys and
+ * per-token values in the INT2 region; the INT4 region holds per-token keys
+ * and values at 4 bits (TriAxialKV page, "Facts": quantizer and page-pool
+ * bullets).
+ *   shape, cfg[num_layers]: in; out: filled on success.
+ *   Errors: INVALID_ARG (null, num_layers out of 1..KVQ_MAX_LAYERS, sizes
+ *   <= 0), UNSUPPORTED (head_dim != 128, group_size != 32, bits not in
+ *   {2,4,8,16}, v_axis != TOKEN, Hq not a multiple of Hkv or G > 16,
+ *   page_tokens not 0 or 16, paged layer not K2V2).
+ */
+int kvq_plan_layers(const kvq_shape *shape, const kvq_layer_cfg *cfg, int32_t num_layers,
+                    kvq_plan *out);
+
+/*
+ * kvq_quantize_append -- append n_new tokens to every request of one layer.
+ * k_new, v_new: device fp16 [batch][Hkv][n_new][128].
+ * Contiguous mode: seq_lens (device int32 [batch]) is each request's length
+ * before the call. Every 32-token group that the new tokens complete is
+ * quantized and packed (asymmetric min/max, group 32: TriAxialKV page,
+ * "Facts", quantizer bullet; keys per-channel or per-token as planned, values
+ * per-token); the tokens past the last full group are kept in fp16 in the
+ * stream's tail record. The call does not advance seq_lens: the caller
+ * does. A stream whose length would pass max_tokens is left unchanged.
+ * Paged mode (pages != NULL): the first int2_add[r] new tokens of request r
+ * (a multiple of 32) are quantized into INT2 page pairs after int2_len[r];
+ * the others, one token at a time, into INT4 pages after int4_len[r]
+ * (TriAxialKV page, "Facts": leftover INT2 tokens go through the INT4
+ * per-token path). The caller advances int2_len/int4_len.
+ *   Errors: INVALID_ARG (null pointers, layer, batch, n_new out of range),
+ *   CAPACITY (n_new > max_tokens), HIP.
+ */
+int kvq_quantize_append(const kvq_plan *plan, int32_t layer, void *cache, const uint16_t *k_new,
+                        const uint16_t *v_new, const int32_t *seq_lens, int32_t batch,
+                        int32_t n_new, const kvq_pages *pages, kvq_stream_t stream);
+
+/* Workspace bytes kvq_decode_attention needs (split partials:
+ * batch * Hq * splits * (128 + 1) fp32). num_splits = 0 means the count the
+ * library would choose. Returns 0 on invalid arguments. */
+size_t kvq_decode_workspace_bytes(const kvq_plan *plan, int32_t batch, int32_t max_seq_len,
+                                  int32_t num_splits);
+
+/* The split count kvq_decode_attention uses for num_splits = 0. */
+int32_t kvq_decode_num_splits(const kvq_plan *plan, int32_t layer, int32_t batch,
+                              int32_t max_seq_len);
+
+/*
+ * kvq_decode_attention -- one decode step of one layer: softmax attention of
+ * q (device fp16 [batch][Hq][128]) over every cached token of each request.
+ * Split-KV flash decoding: each split reads its share of the packed groups,
+ * dequantizes in registers and keeps a running max and sum; a second pass
+ * merges the splits by log-sum-exp (TriAxialKV page, "Facts": flash-decoding
+ * splits merged by online log-sum-exp). The fp16 tail is part of the last
+ * split. Query head h uses KV head h / (Hq / Hkv).
+ *   seq_lens: device [batch] tokens per request (contiguous mode);
+ *   max_seq_len: host upper bound of seq_lens (sizes the grid, no sync);
+ *   softmax_scale: score = scale * q.k (usually 1/sqrt(128));
+ *   out: device [batch][Hq][128], fp16 or fp32 (out_dtype);
+ *   lse_out: device fp32 [batch][Hq] natural-log log-sum-exp, nullable;
+ *   workspace: device, at least kvq_decode_workspace_bytes(...);
+ *   num_splits: 0 = automatic, else 1..1024.
+ * A request with no tokens gets out = 0 and lse = -inf.
+ * Paged mode (pages != NULL): lengths come from pages->int2_len/int4_len and
+ * seq_lens is ignored; max_seq_len bounds int2_len + int4_len.
+ *   Errors: INVALID_ARG, CAPACITY (max_seq_len > capacity), WORKSPACE, HIP.
+ */
+int kvq_decode_attention(const kvq_plan *plan, int32_t layer, const void *cache,
+                         const uint16_t *q, const int32_t *seq_lens, int32_t batch,
+                         int32_t max_seq_len, float softmax_scale, void *out, int32_t out_dtype,
+                         float *lse_out, void *workspace, size_t workspace_bytes,
+                         int32_t num_splits, const kvq_pages *pages, kvq_stream_t stream);
+
+/*
+ * kvq_dequantize -- the cache of one layer back in fp32, for checking:
+ * k_out, v_out: device fp32 [batch][Hkv][max_seq_len][128]; token j of
+ * request r is fmaf(code, scale, zero) for quantized tokens and the stored
+ * fp16 value for tail tokens; rows at or past the request's length are not
+ * written. Paged mode lists INT2 tokens first, then INT4 tokens.
+ *   Errors: INVALID_ARG, CAPACITY, HIP.
+ */
+int kvq_dequantize(const kvq_plan *plan, int32_t layer, const void *cache,
+                   const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float *k_out,
+                   float *v_out, const kvq_pages *pages, kvq_stream_t stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *kvq_last_error(void);
+
+/*
+ * Optional kernel timer (HIP events recorded around each kernel launch, on
+ * the launch stream). kvq_timer_start(capacity) clears and arms it for up to
+ * `capacity` launches per kind; kvq_timer_read(kind, ...) synchronizes the
+ * recorded events and returns the summed milliseconds and the launch count
+ * for a kind (0 = append, 1 = decode split pass, 2 = merge pass);
+ * kvq_timer_stop() disarms it and frees the events.
+ */
+int kvq_timer_start(int32_t capacity);
+int kvq_timer_read(int32_t kind, double *total_ms, int32_t *launches);
+int kvq_timer_stop(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,361 @@
+// kvq_api.cpp -- host side of libkvq: the layer planner, argument checks,
+// launches, the error string and the optional kernel timer. Every function of
+// include/kvq.h is defined here; the kernels live in the .hip files.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return KVQ_OK;
+}
+
+bool valid_bits(int b) { return b == 2 || b == 4 || b == 8 || b == 16; }
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- timer
+
+struct Timer {
+  std::mutex mu;
+  bool armed = false;
+  int capacity = 0;
+  std::vector<hipEvent_t> ev[3][2];
+  int used[3] = {0, 0, 0};
+} g_timer;
+
+void timer_free_locked() {
+  for (int k = 0; k < 3; ++k)
+    for (int i = 0; i < 2; ++i) {
+      for (hipEvent_t e : g_timer.ev[k][i]) (void)hipEventDestroy(e);
+      g_timer.ev[k][i].clear();
+    }
+  g_timer.armed = false;
+  g_timer.capacity = 0;
+  for (int k = 0; k < 3; ++k) g_timer.used[k] = 0;
+}
+
+// Records the start event of a launch of `kind`; returns the slot or -1.
+int timer_begin(int kind, hipStream_t s) {
+  if (!g_timer.armed) return -1;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (!g_timer.armed || g_timer.used[kind] >= g_timer.capacity) return -1;
+  const int slot = g_timer.used[kind]++;
+  (void)hipEventRecord(g_timer.ev[kind][0][slot], s);
+  return slot;
+}
+
+void timer_end(int kind, int slot, hipStream_t s) {
+  if (slot < 0) return;
+  (void)hipEventRecord(g_timer.ev[kind][1][slot], s);
+}
+
+// ----------------------------------------------------------- arguments
+
+int check_plan_layer(const kvq_plan* plan, int32_t layer) {
+  if (!plan) return fail(KVQ_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->num_layers < 1 || plan->num_layers > KVQ_MAX_LAYERS)
+    return fail(KVQ_ERR_INVALID_ARG, "plan has %d layers (not planned?)", plan->num_layers);
+  if (layer < 0 || layer >= plan->num_layers)
+    return fail(KVQ_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, plan->num_layers);
+  return KVQ_OK;
+}
+
+kvq::LayerGeom geom(const kvq_plan* plan, int32_t layer, const void* cache) {
+  const kvq_layer_plan& lp = plan->layers[layer];
+  kvq::LayerGeom g;
+  g.base = (uint8_t*)cache + lp.offset;
+  g.stream_bytes = lp.stream_bytes;
+  g.record_bytes = lp.record_bytes;
+  g.tail_offset = lp.tail_offset;
+  g.groups_cap = (int)lp.groups_cap;
+  g.kb = lp.k_bits;
+  g.vb = lp.v_bits;
+  g.k_token = lp.k_axis == KVQ_AXIS_TOKEN;
+  g.hkv = plan->shape.num_kv_heads;
+  g.hq = plan->shape.num_q_heads;
+  g.g = g.hq / g.hkv;
+  g.max_tokens = plan->shape.max_tokens;
+  return g;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
+  const int64_t streams = (int64_t)batch * plan->shape.num_kv_heads;
+  const int64_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
+  if (nvg <= 0 || streams <= 0) return 1;
+  // aim for ~4 workgroups per CU on 256 CUs, at least 2 groups per split
+  int64_t s = (1024 + streams - 1) / streams;
+  const int64_t max_s = (nvg + 1) / 2;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  if (s > 1024) s = 1024;
+  return (int32_t)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_error.c_str(); }
+
+int kvq_plan_layers(const kvq_shape* shape, const kvq_layer_cfg* cfg, int32_t num_layers, kvq_plan* out) {
+  if (!shape || !cfg || !out) return fail(KVQ_ERR_INVALID_ARG, "null argument");
+  if (num_layers < 1 || num_layers > KVQ_MAX_LAYERS)
+    return fail(KVQ_ERR_INVALID_ARG, "num_layers %d out of range [1, %d]", num_layers, KVQ_MAX_LAYERS);
+  const kvq_shape& s = *shape;
+  if (s.head_dim != KVQ_HEAD_DIM) return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d (only 128)", s.head_dim);
+  if (s.group_size != KVQ_GROUP) return fail(KVQ_ERR_UNSUPPORTED, "group_size %d (only 32)", s.group_size);
+  if (s.num_q_heads <= 0 || s.num_kv_heads <= 0 || s.max_batch <= 0)
+    return fail(KVQ_ERR_INVALID_ARG, "heads and max_batch must be positive");
+  if (s.num_q_heads % s.num_kv_heads != 0)
+    return fail(KVQ_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d", s.num_q_heads,
+                s.num_kv_heads);
+  if (s.num_q_heads / s.num_kv_heads > 16)
+    return fail(KVQ_ERR_UNSUPPORTED, "GQA group %d > 16", s.num_q_heads / s.num_kv_heads);
+  if (s.page_tokens != 0 && s.page_tokens != 16)
+    return fail(KVQ_ERR_UNSUPPORTED, "page_tokens %d (0 or 16)", s.page_tokens);
+  const bool paged = s.page_tokens == 16;
+  if (!paged && s.max_tokens <= 0) return fail(KVQ_ERR_INVALID_ARG, "max_tokens must be positive");
+  if (paged) {
+    if (s.int2_pages < 0 || s.int4_pages < 0 || (s.int2_pages & 1) || s.int2_pages + s.int4_pages <= 0)
+      return fail(KVQ_ERR_INVALID_ARG, "paged pool needs an even int2_pages >= 0 and int4_pages >= 0");
+  }
+  for (int l = 0; l < num_layers; ++l) {
+    const kvq_layer_cfg& c = cfg[l];
+    if (!valid_bits(c.k_bits) || !valid_bits(c.v_bits))
+      return fail(KVQ_ERR_UNSUPPORTED, "layer %d: bits K%d V%d (each of 2, 4, 8, 16)", l, c.k_bits, c.v_bits);
+    if (c.k_axis != KVQ_AXIS_CHANNEL && c.k_axis != KVQ_AXIS_TOKEN)
+      return fail(KVQ_ERR_UNSUPPORTED, "layer %d: k_axis %d", l, c.k_axis);
+    if (c.v_axis != KVQ_AXIS_TOKEN) return fail(KVQ_ERR_UNSUPPORTED, "layer %d: v_axis must be per-token", l);
+    if (paged && !(c.k_bits == 2 && c.v_bits == 2 && c.k_axis == KVQ_AXIS_CHANNEL))
+      return fail(KVQ_ERR_UNSUPPORTED, "layer %d: a paged pool needs K2V2 per-channel keys", l);
+  }
+  std::memset(out, 0, sizeof *out);
+  out->shape = s;
+  out->num_layers = num_layers;
+  uint64_t off = 0;
+  double bits = 0.0;
+  const uint64_t hkv = (uint64_t)s.num_kv_heads;
+  for (int l = 0; l < num_layers; ++l) {
+    const kvq_layer_cfg& c = cfg[l];
+    kvq_layer_plan& lp = out->layers[l];
+    lp.k_bits = c.k_bits;
+    lp.v_bits = c.v_bits;
+    lp.k_axis = c.k_axis;
+    lp.v_axis = c.v_axis;
+    lp.offset = off;
+    lp.record_bytes = kvq::record_bytes(c.k_bits, c.v_bits);
+    if (!paged) {
+      lp.groups_cap = (uint64_t)s.max_tokens / kvq::GS;
+      lp.stream_bytes = lp.groups_cap * lp.record_bytes + kvq::TAIL_BYTES;
+      lp.tail_offset = lp.groups_cap * lp.record_bytes;
+      lp.bytes = (uint64_t)s.max_batch * hkv * lp.stream_bytes;
+      bits += (c.k_bits + c.v_bits) / 2.0;
+    } else {
+      // INT2 page: half of a K2V2 group record per KV head; INT4 page: 16
+      // tokens of per-token K4 and V4 codes plus their meta per KV head.
+      lp.int2_page_bytes = hkv * 2048u;
+      lp.int4_page_bytes = hkv * 3072u;
+      lp.int4_offset = (uint64_t)s.int2_pages * lp.int2_page_bytes;
+      lp.bytes = lp.int4_offset + (uint64_t)s.int4_pages * lp.int4_page_bytes;
+    }
+    off = align_up(off + lp.bytes, 4096);
+  }
+  out->total_bytes = off;
+  if (paged) {
+    const double n = (double)s.int2_pages + (double)s.int4_pages;
+    out->int2_fraction = s.int2_pages / n;
+    out->equiv_bits = 2.0 * out->int2_fraction + 4.0 * (1.0 - out->int2_fraction);
+  } else {
+    out->equiv_bits = bits / num_layers;
+  }
+  return ok();
+}
+
+int kvq_quantize_append(const kvq_plan* plan, int32_t layer, void* cache, const uint16_t* k_new,
+                        const uint16_t* v_new, const int32_t* seq_lens, int32_t batch, int32_t n_new,
+                        const kvq_pages* pages, kvq_stream_t stream) {
+  int st = check_plan_layer(plan, layer);
+  if (st) return st;
+  if (!cache || !k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "null cache or input pointer");
+  if (batch < 0 || batch > plan->shape.max_batch)
+    return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
+  if (n_new < 0) return fail(KVQ_ERR_INVALID_ARG, "n_new %d < 0", n_new);
+  if (pages || plan->shape.page_tokens) return fail(KVQ_ERR_UNSUPPORTED, "paged append is not built yet");
+  if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (n_new > plan->shape.max_tokens)
+    return fail(KVQ_ERR_CAPACITY, "n_new %d > max_tokens %d", n_new, plan->shape.max_tokens);
+  if (batch == 0 || n_new == 0) return ok();
+  kvq::AppendArgs a;
+  a.geo = geom(plan, layer, cache);
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.seq_lens = seq_lens;
+  a.n_new = n_new;
+  hipStream_t s = (hipStream_t)stream;
+  const int slot = timer_begin(0, s);
+  hipError_t e = kvq::launch_append(a, batch, s);
+  timer_end(0, slot, s);
+  return hip_status(e, "append launch");
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_plan* plan, int32_t batch, int32_t max_seq_len, int32_t num_splits) {
+  if (!plan || batch < 0 || max_seq_len < 0 || num_splits < 0 || num_splits > 1024) return 0;
+  const int32_t s = num_splits ? num_splits : auto_splits(plan, batch, max_seq_len);
+  return (size_t)batch * plan->shape.num_q_heads * s * (kvq::D + 1) * sizeof(float);
+}
+
+int32_t kvq_decode_num_splits(const kvq_plan* plan, int32_t layer, int32_t batch, int32_t max_seq_len) {
+  (void)layer;
+  if (!plan || batch < 0 || max_seq_len < 0) return 0;
+  return auto_splits(plan, batch, max_seq_len);
+}
+
+int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache, const uint16_t* q,
+                         const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float softmax_scale,
+                         void* out, int32_t out_dtype, float* lse_out, void* workspace, size_t workspace_bytes,
+                         int32_t num_splits, const kvq_pages* pages, kvq_stream_t stream) {
+  int st = check_plan_layer(plan, layer);
+  if (st) return st;
+  if (!cache || !q || !out) return fail(KVQ_ERR_INVALID_ARG, "null cache, q or out");
+  if (batch < 0 || batch > plan->shape.max_batch)
+    return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
+  if (out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_F32)
+    return fail(KVQ_ERR_INVALID_ARG, "out_dtype %d", out_dtype);
+  if (num_splits < 0 || num_splits > 1024) return fail(KVQ_ERR_INVALID_ARG, "num_splits %d", num_splits);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+  if (pages || plan->shape.page_tokens) return fail(KVQ_ERR_UNSUPPORTED, "paged decode is not built yet");
+  if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (max_seq_len > plan->shape.max_tokens)
+    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > max_tokens %d", max_seq_len, plan->shape.max_tokens);
+  if (batch == 0) return ok();
+  const int32_t splits = num_splits ? num_splits : auto_splits(plan, batch, max_seq_len);
+  const size_t need = (size_t)batch * plan->shape.num_q_heads * splits * (kvq::D + 1) * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
+  kvq::DecodeArgs a;
+  a.geo = geom(plan, layer, cache);
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.splits = splits;
+  a.groups_per_split = nvg > 0 ? (nvg + splits - 1) / splits : 0;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.part_o = (float*)workspace;
+  a.part_lse = a.part_o + (size_t)batch * plan->shape.num_q_heads * splits * kvq::D;
+  hipStream_t s = (hipStream_t)stream;
+  int slot = timer_begin(1, s);
+  hipError_t e = kvq::launch_decode_split(a, batch, s);
+  timer_end(1, slot, s);
+  if (e != hipSuccess) return hip_status(e, "decode split launch");
+  kvq::MergeArgs m;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.splits = splits;
+  m.rows = batch * plan->shape.num_q_heads;
+  m.out = out;
+  m.out_f32 = out_dtype == KVQ_OUT_F32;
+  m.lse_out = lse_out;
+  slot = timer_begin(2, s);
+  e = kvq::launch_merge(m, s);
+  timer_end(2, slot, s);
+  return hip_status(e, "merge launch");
+}
+
+int kvq_dequantize(const kvq_plan* plan, int32_t layer, const void* cache, const int32_t* seq_lens, int32_t batch,
+                   int32_t max_seq_len, float* k_out, float* v_out, const kvq_pages* pages, kvq_stream_t stream) {
+  int st = check_plan_layer(plan, layer);
+  if (st) return st;
+  if (!cache || !k_out || !v_out) return fail(KVQ_ERR_INVALID_ARG, "null cache or output");
+  if (batch < 0 || batch > plan->shape.max_batch)
+    return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
+  if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+  if (pages || plan->shape.page_tokens) return fail(KVQ_ERR_UNSUPPORTED, "paged dequantize is not built yet");
+  if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (max_seq_len > plan->shape.max_tokens)
+    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > max_tokens %d", max_seq_len, plan->shape.max_tokens);
+  if (batch == 0 || max_seq_len == 0) return ok();
+  kvq::DequantArgs a;
+  a.geo = geom(plan, layer, cache);
+  a.seq_lens = seq_lens;
+  a.max_seq_len = max_seq_len;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  return hip_status(kvq::launch_dequant(a, batch, (hipStream_t)stream), "dequantize launch");
+}
+
+int kvq_timer_start(int32_t capacity) {
+  if (capacity <= 0 || capacity > (1 << 20)) return fail(KVQ_ERR_INVALID_ARG, "timer capacity %d", capacity);
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  timer_free_locked();
+  for (int k = 0; k < 3; ++k)
+    for (int i = 0; i < 2; ++i) {
+      g_timer.ev[k][i].resize(capacity);
+      for (int n = 0; n < capacity; ++n) {
+        hipError_t e = hipEventCreate(&g_timer.ev[k][i][n]);
+        if (e != hipSuccess) {
+          g_timer.ev[k][i].resize(n);
+          timer_free_locked();
+          return fail(KVQ_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+        }
+      }
+    }
+  g_timer.capacity = capacity;
+  g_timer.armed = true;
+  return ok();
+}
+
+int kvq_timer_read(int32_t kind, double* total_ms, int32_t* launches) {
+  if (kind < 0 || kind > 2 || !total_ms || !launches) return fail(KVQ_ERR_INVALID_ARG, "bad timer read arguments");
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  double sum = 0.0;
+  const int n = g_timer.used[kind];
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer.ev[kind][1][i]);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_timer.ev[kind][0][i], g_timer.ev[kind][1][i]);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return ok();
+}
+
+int kvq_timer_stop(void) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  timer_free_locked();
+  return ok();
+}
+
+}  // extern "C"

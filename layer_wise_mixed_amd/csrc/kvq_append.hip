@@ -1,0 +1,224 @@
+// kvq_append.hip -- quantize-and-pack on append, and the checking dequantizer.
+//
+// Quantizer (TriAxialKV page, "Facts", quantizer bullet: asymmetric groupwise,
+// group size 32): scale = (max - min) / (2^b - 1) in fp32, zero = min,
+// code = clamp(rint((x - zero) / scale), 0, 2^b - 1) with IEEE division and
+// round-half-even; a constant group gets scale 0 and codes 0. Keys are grouped
+// per channel over 32 tokens (KVTuner summary page, "Facts": keys have
+// channel-wise outliers) or per token over 32 channels; values per token.
+// Tokens that do not fill a group stay fp16 in the stream's tail record.
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+__device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+__device__ inline uint16_t tail_get(const uint8_t* rec, bool is_v, int j, int c) {
+  int lane, e;
+  if (is_v) v_site(j, c, &lane, &e); else k_site(j, c, &lane, &e);
+  const uint8_t* blk = rec + (is_v ? 8192 : 0);
+  return *(const uint16_t*)(blk + word_offset(lane, e >> 1) + (e & 1) * 2);
+}
+
+__device__ inline void tail_put(uint8_t* rec, bool is_v, int j, int c, uint16_t x) {
+  int lane, e;
+  if (is_v) v_site(j, c, &lane, &e); else k_site(j, c, &lane, &e);
+  uint8_t* blk = rec + (is_v ? 8192 : 0);
+  *(uint16_t*)(blk + word_offset(lane, e >> 1) + (e & 1) * 2) = x;
+}
+
+// One group of 32 values x[i * stride]; writes codes[i * cstride], returns scale/zero.
+__device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint16_t* codes,
+                                  int cstride, float* scale, float* zero) {
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll 8
+  for (int i = 0; i < GS; ++i) {
+    const float v = h2f(x[i * stride]);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  const float levels = (float)((1 << bits) - 1);
+  const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
+  *scale = s;
+  *zero = mn;
+#pragma unroll 8
+  for (int i = 0; i < GS; ++i) {
+    uint16_t code = 0;
+    if (s != 0.0f) {
+      const float t = __fdiv_rn(__fsub_rn(h2f(x[i * stride]), mn), s);
+      float r = rintf(t);
+      r = fminf(fmaxf(r, 0.0f), levels);
+      code = (uint16_t)r;
+    }
+    codes[i * cstride] = code;
+  }
+}
+
+// Write the 512*bits bytes of a code block from codes[32][128] (token, channel).
+__device__ inline void pack_block(uint8_t* blk, const uint16_t (*codes)[D], int bits, bool is_v, int tid,
+                                  int nthreads) {
+  const int per_word = 32 / bits;
+  const int nwords = 128 * bits;
+  for (int W = tid; W < nwords; W += nthreads) {
+    const int lane = (W & 255) >> 2;
+    const int w = (W >> 8) * 4 + (W & 3);
+    uint32_t word = 0;
+    for (int p = 0; p < per_word; ++p) {
+      const int e = w * per_word + p;
+      int j, c;
+      if (is_v) v_inverse(lane, e, &j, &c); else k_inverse(lane, e, &j, &c);
+      const uint32_t code = codes[j][c];
+      word |= code << ((p & 1) * 16 + (p >> 1) * bits);
+    }
+    *(uint32_t*)(blk + (size_t)W * 4) = word;
+  }
+}
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  __shared__ uint16_t xs[2][GS][D];
+  __shared__ uint16_t cs[2][GS][D];
+  const LayerGeom& g = a.geo;
+  const int tid = threadIdx.x;
+  const int y = blockIdx.x;
+  const int sigma = blockIdx.y;
+  const int r = sigma / g.hkv;
+  const int L0 = a.seq_lens[r];
+  const int L1 = L0 + a.n_new;
+  if (L0 < 0 || L1 > g.max_tokens) return;  // would pass the planned capacity
+  const int m0 = L0 / GS;
+  const int F = L1 / GS - m0;  // groups this call completes
+  uint8_t* stream = g.base + (size_t)sigma * g.stream_bytes;
+  uint8_t* tail = stream + g.tail_offset;
+  const uint16_t* kn = a.k_new + (size_t)sigma * a.n_new * D;
+  const uint16_t* vn = a.v_new + (size_t)sigma * a.n_new * D;
+
+  if (y < F) {
+    const int m = m0 + y;
+    for (int idx = tid; idx < GS * D; idx += blockDim.x) {
+      const int i = idx >> 7, c = idx & 127;
+      const int t = GS * m + i;
+      uint16_t kv, vv;
+      if (t < L0) {  // earlier tokens of this group wait in the tail
+        kv = tail_get(tail, false, i, c);
+        vv = tail_get(tail, true, i, c);
+      } else {
+        kv = kn[(size_t)(t - L0) * D + c];
+        vv = vn[(size_t)(t - L0) * D + c];
+      }
+      xs[0][i][c] = kv;
+      xs[1][i][c] = vv;
+    }
+    __syncthreads();
+    uint8_t* rec = stream + (size_t)m * g.record_bytes;
+    const RecordParts parts = record_parts(g.kb, g.vb);
+    float* kmeta = (float*)(rec + parts.kmeta);
+    float* vmeta = (float*)(rec + parts.vmeta);
+    if (tid < 128) {
+      if (g.kb == 16) {
+        for (int i = 0; i < GS; ++i) cs[0][i][tid] = xs[0][i][tid];
+      } else if (!g.k_token) {
+        const int c = tid;
+        float s, z;
+        quantize32(&xs[0][0][c], D, g.kb, &cs[0][0][c], D, &s, &z);
+        kmeta[meta_channel(c)] = s;
+        kmeta[128 + meta_channel(c)] = z;
+      } else {
+        const int j = tid >> 2, n = tid & 3;
+        float s, z;
+        quantize32(&xs[0][j][32 * n], 1, g.kb, &cs[0][j][32 * n], 1, &s, &z);
+        kmeta[meta_token(j, n)] = s;
+        kmeta[128 + meta_token(j, n)] = z;
+      }
+    } else {
+      const int t2 = tid - 128;
+      if (g.vb == 16) {
+        for (int i = 0; i < GS; ++i) cs[1][i][t2] = xs[1][i][t2];
+      } else {
+        const int j = t2 >> 2, n = t2 & 3;
+        float s, z;
+        quantize32(&xs[1][j][32 * n], 1, g.vb, &cs[1][j][32 * n], 1, &s, &z);
+        vmeta[meta_token(j, n)] = s;
+        vmeta[128 + meta_token(j, n)] = z;
+      }
+    }
+    __syncthreads();
+    pack_block(rec, cs[0], g.kb, false, tid, blockDim.x);
+    pack_block(rec + parts.vcode, cs[1], g.vb, true, tid, blockDim.x);
+  }
+  if (y == 0) {
+    __syncthreads();  // the flush above has read the old tail slots
+    const int tstart = max(L0, GS * (L1 / GS));
+    const int nt = L1 - tstart;
+    for (int idx = tid; idx < nt * D; idx += blockDim.x) {
+      const int t = tstart + (idx >> 7), c = idx & 127;
+      const int slot = t % GS;
+      tail_put(tail, false, slot, c, kn[(size_t)(t - L0) * D + c]);
+      tail_put(tail, true, slot, c, vn[(size_t)(t - L0) * D + c]);
+    }
+  }
+}
+
+__device__ inline float read_elem(const uint8_t* rec, const RecordParts& parts, int kb, int vb, int k_token,
+                                  bool is_v, int j, int c) {
+  const int bits = is_v ? vb : kb;
+  const uint8_t* blk = rec + (is_v ? parts.vcode : 0);
+  int lane, e;
+  if (is_v) v_site(j, c, &lane, &e); else k_site(j, c, &lane, &e);
+  uint32_t off;
+  int sh;
+  code_site(lane, e, bits, &off, &sh);
+  const uint32_t word = *(const uint32_t*)(blk + off);
+  if (bits == 16) return h2f((uint16_t)(word >> sh));
+  const uint32_t code = (word >> sh) & ((1u << bits) - 1u);
+  const float* meta = (const float*)(rec + (is_v ? parts.vmeta : parts.kmeta));
+  const int mi = (is_v || k_token) ? meta_token(j, c >> 5) : meta_channel(c);
+  return fmaf((float)code, meta[mi], meta[128 + mi]);
+}
+
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
+  const LayerGeom& g = a.geo;
+  const int m = blockIdx.x;
+  const int sigma = blockIdx.y;
+  const int r = sigma / g.hkv;
+  const int L = a.seq_lens[r];
+  if (L < 0 || L > g.max_tokens) return;
+  const int lw = min(L, a.max_seq_len);  // rows past max_seq_len have no room in k_out
+  const int nq = L / GS;
+  if (m * GS >= lw) return;
+  const uint8_t* stream = g.base + (size_t)sigma * g.stream_bytes;
+  const bool full = m < nq;
+  const uint8_t* rec = full ? stream + (size_t)m * g.record_bytes : stream + g.tail_offset;
+  const int kb = full ? g.kb : 16, vb = full ? g.vb : 16;
+  const RecordParts parts = record_parts(kb, vb);
+  for (int idx = threadIdx.x; idx < GS * D; idx += blockDim.x) {
+    const int j = idx >> 7, c = idx & 127;
+    const int t = m * GS + j;
+    if (t >= lw) continue;
+    const size_t o = ((size_t)sigma * a.max_seq_len + t) * D + c;
+    a.k_out[o] = read_elem(rec, parts, kb, vb, g.k_token, false, j, c);
+    a.v_out[o] = read_elem(rec, parts, kb, vb, g.k_token, true, j, c);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s) {
+  const int y = a.n_new > 0 ? (a.n_new + GS - 1) / GS : 0;
+  if (y == 0 || batch == 0) return hipSuccess;
+  dim3 grid(y, batch * a.geo.hkv);
+  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s) {
+  const int y = (a.max_seq_len + GS - 1) / GS;
+  if (y == 0 || batch == 0) return hipSuccess;
+  dim3 grid(y, batch * a.geo.hkv);
+  hipLaunchKernelGGL(dequant_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,150 @@
+// kvq_internal.h -- device-side layout helpers and launch interfaces shared by
+// the HIP translation units of libkvq. Not part of the public ABI.
+//
+// Cache layout (this library's own; no page prescribes one). A 32-token group
+// of one (layer, request, KV head) stream is one record:
+//   [K codes 512*bK B][V codes 512*bV B][K meta 1 KiB if bK<16][V meta 1 KiB if bV<16]
+// A code block is 64 lanes x (8*b bytes); lane word w sits at byte
+// (w/4)*1024 + lane*16 + (w%4)*4, so word w of all 64 lanes is one coalesced
+// 1 KiB row and a lane's words 4k..4k+3 are one 16-byte load. Inside a word,
+// even code positions fill bits 0..15 and odd positions bits 16..31, so that
+// a pair of consecutive positions unpacks to the two halves of a register.
+// Lane/position of token j (0..31) and channel c (0..127):
+//   K: lane 16*((c/8)%4) + j%16, position 32*(j/16) + 8*(c/32) + c%8
+//   V: lane 16*((j%16)/4) + c%16, position 8*(c/16) + 4*(j/16) + j%4
+// which are the operand layouts of a 16x16x32 f16 MFMA with tokens as rows of
+// the score tile (K) and tokens as the reduction index of the P.V tile (V).
+// Meta: 128 fp32 scales then 128 fp32 zeros, per-channel index
+// 32*((c/8)%4) + 8*(c/32) + c%8, per-token index 32*n + kappa(j),
+// kappa(j) = 8*((j%16)/4) + 4*(j/16) + j%4.
+// A stream is groups_cap records then one tail record in the K16V16 format.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;
+constexpr int GS = 32;
+constexpr int TAIL_BYTES = 16384;
+constexpr int META_BYTES = 1024;
+
+__host__ __device__ inline uint32_t word_offset(int lane, int w) {
+  return (uint32_t)(w >> 2) * 1024u + (uint32_t)lane * 16u + (uint32_t)(w & 3) * 4u;
+}
+
+// byte offset of the word holding position e of `lane`, and the bit shift
+__host__ __device__ inline void code_site(int lane, int e, int bits, uint32_t* off, int* shift) {
+  const int per_word = 32 / bits;
+  const int w = e / per_word;
+  const int p = e - w * per_word;
+  *off = word_offset(lane, w);
+  *shift = (p & 1) * 16 + (p >> 1) * bits;
+}
+
+__host__ __device__ inline void k_site(int j, int c, int* lane, int* e) {
+  *lane = 16 * ((c >> 3) & 3) + (j & 15);
+  *e = 32 * (j >> 4) + 8 * (c >> 5) + (c & 7);
+}
+
+__host__ __device__ inline void v_site(int j, int c, int* lane, int* e) {
+  *lane = 16 * ((j & 15) >> 2) + (c & 15);
+  *e = 8 * (c >> 4) + 4 * (j >> 4) + (j & 3);
+}
+
+// inverse maps: (lane, position) -> (token, channel)
+__host__ __device__ inline void k_inverse(int lane, int e, int* j, int* c) {
+  const int a = lane >> 4, r = lane & 15;
+  *j = 16 * (e >> 5) + r;
+  *c = 32 * ((e >> 3) & 3) + 8 * a + (e & 7);
+}
+
+__host__ __device__ inline void v_inverse(int lane, int e, int* j, int* c) {
+  const int a = lane >> 4, r = lane & 15;
+  const int ip = e & 7;
+  *c = 16 * (e >> 3) + r;
+  *j = 16 * (ip >> 2) + 4 * a + (ip & 3);
+}
+
+__host__ __device__ inline int meta_channel(int c) { return 32 * ((c >> 3) & 3) + 8 * (c >> 5) + (c & 7); }
+
+__host__ __device__ inline int kappa(int j) { return 8 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3); }
+
+__host__ __device__ inline int meta_token(int j, int n) { return 32 * n + kappa(j); }
+
+__host__ __device__ inline uint32_t record_bytes(int kb, int vb) {
+  return 512u * kb + 512u * vb + (kb < 16 ? META_BYTES : 0) + (vb < 16 ? META_BYTES : 0);
+}
+
+// byte offsets of the four parts of a record
+struct RecordParts {
+  uint32_t vcode, kmeta, vmeta;
+};
+
+__host__ __device__ inline RecordParts record_parts(int kb, int vb) {
+  RecordParts p;
+  p.vcode = 512u * kb;
+  p.kmeta = p.vcode + 512u * vb;
+  p.vmeta = p.kmeta + (kb < 16 ? META_BYTES : 0);
+  return p;
+}
+
+// ------------------------------------------------------------ launch args
+
+struct LayerGeom {
+  uint8_t* base;          // layer region
+  uint64_t stream_bytes;  // per (request, KV head)
+  uint64_t record_bytes;
+  uint64_t tail_offset;
+  int groups_cap;
+  int kb, vb, k_token;
+  int hkv, hq, g;
+  int max_tokens;
+};
+
+struct AppendArgs {
+  LayerGeom geo;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* seq_lens;
+  int n_new;
+};
+
+struct DequantArgs {
+  LayerGeom geo;
+  const int32_t* seq_lens;
+  int max_seq_len;
+  float* k_out;
+  float* v_out;
+};
+
+struct DecodeArgs {
+  LayerGeom geo;
+  const uint16_t* q;
+  const int32_t* seq_lens;
+  int splits;
+  int groups_per_split;  // virtual groups (32 tokens; the tail counts as one)
+  float scale_log2;      // softmax_scale * log2(e)
+  float* part_o;         // [batch][Hq][splits][128]
+  float* part_lse;       // [batch][Hq][splits]  natural log
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  int splits;
+  int rows;  // batch * Hq
+  void* out;
+  int out_f32;
+  float* lse_out;
+};
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s);
+hipError_t launch_decode_split(const DecodeArgs& a, int batch, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
+}  // namespace kvq

@@ -135,9 +135,16 @@ def values_fp16(seed, layer, requests, heads, tok_start, n_tok, *, head_dim=128,
 
 
 def queries_fp16(seed, layer, step, batch, num_q_heads, *, head_dim=128, device="cpu") -> torch.Tensor:
-    """q [batch, num_q_heads, head_dim] for one decode step of one layer."""
-    x = normal_fp16(seed, T_Q, layer * 65536 + step, range(batch), range(num_q_heads), 0, 1, head_dim, device)
+    """q [batch, num_q_heads, head_dim] of one decode step of one layer."""
+    x = normal_fp16(seed, T_Q, layer, range(batch), range(num_q_heads), step, 1, head_dim, device)
     return x[:, :, 0, :].contiguous()
+
+
+def queries_steps_fp16(seed, layer, batch, num_q_heads, step_start, n_steps, *, head_dim=128,
+                       device="cpu") -> torch.Tensor:
+    """q [batch, num_q_heads, n_steps, head_dim] of consecutive decode steps of one layer
+    (step s equals queries_fp16(seed, layer, s, ...))."""
+    return normal_fp16(seed, T_Q, layer, range(batch), range(num_q_heads), step_start, n_steps, head_dim, device)
 
 
 def seeded_choice(seed: int, tensor: int, n: int, k: int, salt: int = 0) -> list[int]:
