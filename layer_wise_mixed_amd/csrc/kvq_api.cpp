@@ -58,19 +58,15 @@ void timer_free_locked() {
   for (int k = 0; k < 3; ++k) g_timer.used[k] = 0;
 }
 
-// Records the start event of a launch of `kind`; returns the slot or -1.
-int timer_begin(int kind, hipStream_t s) {
-  if (!g_timer.armed) return -1;
+// Event pair for the next launch of `kind` if the timer is armed and has room.
+bool timer_slot(int kind, kvq::EventPair* ev) {
+  if (!g_timer.armed) return false;
   std::lock_guard<std::mutex> lk(g_timer.mu);
-  if (!g_timer.armed || g_timer.used[kind] >= g_timer.capacity) return -1;
+  if (!g_timer.armed || g_timer.used[kind] >= g_timer.capacity) return false;
   const int slot = g_timer.used[kind]++;
-  (void)hipEventRecord(g_timer.ev[kind][0][slot], s);
-  return slot;
-}
-
-void timer_end(int kind, int slot, hipStream_t s) {
-  if (slot < 0) return;
-  (void)hipEventRecord(g_timer.ev[kind][1][slot], s);
+  ev->start = g_timer.ev[kind][0][slot];
+  ev->stop = g_timer.ev[kind][1][slot];
+  return true;
 }
 
 // ----------------------------------------------------------- arguments
@@ -221,10 +217,9 @@ int kvq_quantize_append(const kvq_plan* plan, int32_t layer, void* cache, const 
   a.seq_lens = seq_lens;
   a.n_new = n_new;
   hipStream_t s = (hipStream_t)stream;
-  const int slot = timer_begin(0, s);
-  hipError_t e = kvq::launch_append(a, batch, s);
-  timer_end(0, slot, s);
-  return hip_status(e, "append launch");
+  kvq::EventPair ev;
+  const bool timed = timer_slot(0, &ev);
+  return hip_status(kvq::launch_append(a, batch, s, timed ? &ev : nullptr), "append launch");
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_plan* plan, int32_t batch, int32_t max_seq_len, int32_t num_splits) {
@@ -273,9 +268,9 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   a.part_o = (float*)workspace;
   a.part_lse = a.part_o + (size_t)batch * plan->shape.num_q_heads * splits * kvq::D;
   hipStream_t s = (hipStream_t)stream;
-  int slot = timer_begin(1, s);
-  hipError_t e = kvq::launch_decode_split(a, batch, s);
-  timer_end(1, slot, s);
+  kvq::EventPair ev;
+  bool timed = timer_slot(1, &ev);
+  hipError_t e = kvq::launch_decode_split_mfma(a, batch, s, timed ? &ev : nullptr);
   if (e != hipSuccess) return hip_status(e, "decode split launch");
   kvq::MergeArgs m;
   m.part_o = a.part_o;
@@ -285,9 +280,8 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   m.out = out;
   m.out_f32 = out_dtype == KVQ_OUT_F32;
   m.lse_out = lse_out;
-  slot = timer_begin(2, s);
-  e = kvq::launch_merge(m, s);
-  timer_end(2, slot, s);
+  timed = timer_slot(2, &ev);
+  e = kvq::launch_merge(m, s, timed ? &ev : nullptr);
   return hip_status(e, "merge launch");
 }
 

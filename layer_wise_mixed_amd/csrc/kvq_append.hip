@@ -205,12 +205,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 
 }  // namespace
 
-hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s) {
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev) {
   const int y = a.n_new > 0 ? (a.n_new + GS - 1) / GS : 0;
   if (y == 0 || batch == 0) return hipSuccess;
-  dim3 grid(y, batch * a.geo.hkv);
-  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_timed(append_kernel, dim3(y, batch * a.geo.hkv), dim3(256), s, ev, a);
 }
 
 hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s) {

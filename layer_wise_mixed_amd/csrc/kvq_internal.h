@@ -20,6 +20,7 @@
 // A stream is groups_cap records then one tail record in the K16V16 format.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -142,9 +143,25 @@ struct MergeArgs {
   float* lse_out;
 };
 
-hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s);
+// Launches. When `ev` is given, its two events are bound to the kernel's own
+// dispatch (start and end of the kernel), for the optional timer.
+struct EventPair {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s);
-hipError_t launch_decode_split(const DecodeArgs& a, int batch, hipStream_t s);
-hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_decode_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s, const EventPair* ev);
+
+// kernel launch with optional dispatch-bound events
+template <typename K, typename A>
+inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, const EventPair* ev, const A& args) {
+  if (ev && ev->start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev->start, ev->stop, 0, args);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args);
+  return hipGetLastError();
+}
 
 }  // namespace kvq
