@@ -234,6 +234,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -248,8 +251,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    kvq.load()
     torch.cuda.set_device(0)
+    if args.copy_calibrate:
+        n = args.copy_calibrate
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+    kvq.load()
     t_setup = time.perf_counter()
     wl = Workload(args.workload, seed=args.seed, num_splits=args.splits)
     K = args.steps if args.steps is not None else wl.C

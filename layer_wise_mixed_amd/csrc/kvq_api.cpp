@@ -107,9 +107,10 @@ int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
   const int64_t streams = (int64_t)batch * plan->shape.num_kv_heads;
   const int64_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
   if (nvg <= 0 || streams <= 0) return 1;
-  // aim for ~4 workgroups per CU on 256 CUs, at least 2 groups per split
-  int64_t s = (1024 + streams - 1) / streams;
-  const int64_t max_s = (nvg + 1) / 2;
+  // 4-wave workgroups: aim for ~512 of them (2 per CU on 256 CUs), but keep
+  // at least 8 groups (2 per wave) in each split
+  int64_t s = (512 + streams - 1) / streams;
+  const int64_t max_s = nvg / 8 > 1 ? nvg / 8 : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   if (s > 1024) s = 1024;
@@ -267,11 +268,15 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.part_o = (float*)workspace;
   a.part_lse = a.part_o + (size_t)batch * plan->shape.num_q_heads * splits * kvq::D;
+  a.out = out;
+  a.out_f32 = out_dtype == KVQ_OUT_F32;
+  a.lse_out = lse_out;
   hipStream_t s = (hipStream_t)stream;
   kvq::EventPair ev;
   bool timed = timer_slot(1, &ev);
   hipError_t e = kvq::launch_decode_split_mfma(a, batch, s, timed ? &ev : nullptr);
   if (e != hipSuccess) return hip_status(e, "decode split launch");
+  if (splits == 1) return ok();  // the split pass wrote the final output
   kvq::MergeArgs m;
   m.part_o = a.part_o;
   m.part_lse = a.part_lse;

@@ -131,6 +131,9 @@ struct DecodeArgs {
   float scale_log2;      // softmax_scale * log2(e)
   float* part_o;         // [batch][Hq][splits][128]
   float* part_lse;       // [batch][Hq][splits]  natural log
+  void* out;             // with one split the split pass writes the final output ...
+  int out_f32;
+  float* lse_out;        // ... and log-sum-exp (nullable)
 };
 
 struct MergeArgs {

@@ -1,32 +1,39 @@
 // kvq_split_mfma.hip -- the split pass of decode attention on CDNA4 matrix cores.
 //
-// One workgroup (4 waves) per (split, KV head, request); each wave walks every
-// fourth 32-token group of the split and keeps its own running max / sum /
-// output, and the four are combined through LDS at the end. Per group:
+// One workgroup (4 waves) per (split, KV head, request). Wave w walks groups
+// w, w+4, w+8, ... of the split (32 tokens each) with the next group's loads in
+// flight, keeps its own running max / sum / output, and the four waves are
+// combined through LDS at the end. With a single split the combine writes the
+// final output and log-sum-exp directly; otherwise it writes the split's
+// partial for the merge pass. Per group:
 //
 //  scores  S[token][col] = sum_ch A[token][ch] * B[ch][col]   (two 16x16x32 f16 MFMA tiles)
-//          A = the packed key codes, fed to the MFMA as fp16 *denormals* (the code
-//              bits, shifted to the top of the fp16 mantissa, so a b-bit code x is
-//              the exact value x * 2^(-14-b); unpacking is one shift and one mask
-//              per register);
-//          B = q' * scale_k for per-channel keys (q' = q * softmax_scale * log2 e),
-//              split into an fp16 high part and an fp16 low part, each its own
-//              MFMA, so the product keeps ~22 significant bits;
+//          A = the packed key codes, fed to the MFMA as fp16 denormals: the code
+//              bits sit at the top of the fp16 mantissa, so a b-bit code x is the
+//              exact value x * 2^(-14-b) (one shift and one mask per register);
+//          B = q' * scale_k (q' = q * softmax_scale * log2 e; per-channel keys),
+//              as an fp16 high part and a 2^11-scaled fp16 low part, each with
+//              its own accumulator, so the product keeps ~22 significant bits;
 //          score = S * 2^(14+b) + sum_ch q'_ch * zero_ch.
-//  softmax exp2 of (score - running max), lazily rescaled when the max grows.
+//  softmax exp2 of (score - running max), rescaled lazily when the max grows.
 //  output  O^T[ch][col] += sum_tok V[tok][ch] * Pt[tok][col]  (eight 16x16x32 MFMA tiles)
-//          with V the value codes as denormals again and Pt = p * scale_v (hi and
-//          lo fp16 parts); the zero-point term sum_tok p * zero_v is kept on the side.
+//          V: the value codes as denormals again, Pt = p * scale_v (high and
+//          2^11-scaled low parts); the zero-point term sum_tok p * zero_v is
+//          kept on the side.
 //
-// The column index of the B operand and of the outputs carries the query row g of
-// the GQA group (col % G) and, on the output side, a 32-channel group of the
-// values (col / G), because value scales are per (token, channel group).
-// The token order inside a group follows the cache layout: the score tile rows
-// land in exactly the registers the P.V tile needs as its reduction index, so
-// no data moves between lanes between the two products.
+// Columns. The 16 columns of the 16x16 tiles carry (query row g of the GQA
+// group = col % G, slot = col / G). On the output side the slot is a 32-channel
+// group of the values (value scales are per token and channel group); with
+// NS = min(4, 16/G) slots, 4/NS passes cover the four channel groups. On the
+// score side of per-channel keys the slot is one of the next NS groups of the
+// wave: the B operand q' * scale_k is built once for NS groups, each group's
+// scores come out in the columns of its slot, and one ds_bpermute per score
+// hands them to the lanes of the other slots.
 //
-// The fp16 tail (tokens that do not fill a group) is processed first by the
-// wave that owns it, in true units, with invalid token slots masked to zero.
+// The token order inside a group follows the cache layout: the score-tile rows
+// land in exactly the registers the P.V tile needs as its reduction index.
+// The fp16 tail (tokens that do not fill a group) is processed first, in true
+// units, by the wave that owns it, with invalid token slots masked.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -41,17 +48,17 @@ constexpr int kWaves = 4;
 
 __device__ inline f4_t mfma(h8_t a, h8_t b, f4_t c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-// The 8 codes at positions 8u..8u+7 of a lane's sequence as an MFMA operand:
-// consecutive position pairs become the two fp16 halves of one register. A
-// b-bit code x goes to mantissa bits 10-b .. 9 of an fp16 denormal, i.e. the
-// exact value x * 2^(-14-b) (code_scale<b>() undoes it). Keeping the code at
-// the top of the mantissa matters: the matrix cores add products of tiny
-// denormals with visibly less precision than the same products placed high.
+// 2^(14+b): the value of code 1 as the MFMA sees it is 2^(-14-b).
 template <int B>
 __device__ constexpr float code_scale() {
-  return B == 2 ? 65536.0f : B == 4 ? 262144.0f : B == 8 ? 4194304.0f : 1.0f;  // 2^(14+B)
+  return B == 2 ? 65536.0f : B == 4 ? 262144.0f : B == 8 ? 4194304.0f : 1.0f;
 }
 
+// The 8 codes at positions 8u..8u+7 of a lane's sequence as an MFMA operand:
+// consecutive position pairs become the two fp16 halves of one register, each
+// code at mantissa bits 10-b .. 9 of an fp16 denormal. Keeping the code at the
+// top of the mantissa matters: the matrix cores add products of tiny
+// denormals with visibly less precision than the same products placed high.
 template <int B>
 __device__ inline h8_t unpack8(const uint32_t* w, int u) {
   u4_t r;
@@ -102,9 +109,8 @@ __device__ inline void load_codes(const uint8_t* blk, int lane, uint32_t* w) {
   }
 }
 
-// element i of (hi, lo): the fp16 rounding of x, and what it missed scaled by 2^11
-// (exact), so that the low part stays in the normal fp16 range whenever x does;
-// products with hi and with lo accumulate separately and meet as hi + lo * 2^-11.
+// element i of (hi, lo): the fp16 rounding of x, and what it missed scaled by
+// 2^11 (exact), so the low part stays in the normal fp16 range whenever x does.
 constexpr float kLoUp = 2048.0f;
 constexpr float kLoDown = 1.0f / 2048.0f;
 
@@ -132,21 +138,24 @@ __device__ inline float max_lane_groups(float x) {
   return x;
 }
 
+__device__ inline float bpermute(int addr, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, v)));
+}
+
 struct Lane {
-  int lane, la, c16, gcol, ns, NS;
+  int lane, la, gcol, slot;
   bool col_ok;
-  float qv[32];  // q' of the lane's column for channels 32 s + 8 la + i, index 8 s + i
+  float qv[32];  // q' of the lane's row for channels 32 s + 8 la + i, index 8 s + i
   float qn[4];   // per 32-channel group sums of q' (per-token keys)
 };
 
 struct Acc {
-  f4_t o[8], ol[8];  // P.V products with the high and with the (2^11-scaled) low parts of P
+  f4_t o[8], ol[8];  // P.V with the high and with the (2^11-scaled) low parts of Pt
   float m, lpart, zpart[4];
 };
 
-// One 32-token group. KB/VB: code widths (16 = fp16 values, as in the tail);
-// meta: this wave's LDS copy of the group's K meta (256 floats) then V meta.
-// q' as hi/lo fp16 B operands (keys without a per-channel scale)
+// B operand of q' alone (keys without per-channel scale: fp16 tail, 16-bit
+// and per-token keys)
 __device__ inline void q_operands(const Lane& ln, h8_t* qh, h8_t* ql) {
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -154,38 +163,31 @@ __device__ inline void q_operands(const Lane& ln, h8_t* qh, h8_t* ql) {
     for (int i = 0; i < 8; ++i) set_hi_lo(qh[s], ql[s], i, ln.qv[8 * s + i]);
 }
 
-template <int KB, int VB, bool KTOK, bool TAIL>
-__device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t* vw, const float* meta, int ntok,
-                                              const Lane& ln, const h8_t* qh, const h8_t* ql, Acc& acc) {
-  float sc[2][4];
-  // ---------------------------------------------------------------- scores
-  if constexpr (KB == 16) {
+// B operand q' * scale_k of per-channel keys for the group of this lane's slot,
+// and beta = sum over all 128 channels of q' * zero_k for the lane's column.
+__device__ inline float k_operands(const Lane& ln, const float* kmeta, h8_t* bh, h8_t* bl) {
+  const float* ks = kmeta + 32 * ln.la;
+  float beta = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f4_t c = {0.f, 0.f, 0.f, 0.f}, cl = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const h8_t A = unpack8<16>(kw, 4 * t + s);
-        c = mfma(A, qh[s], c);
-        cl = mfma(A, ql[s], cl);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[t][i] = fmaf(cl[i], kLoDown, c[i]);
+    for (int i = 0; i < 8; ++i) {
+      set_hi_lo(bh[s], bl[s], i, ln.qv[8 * s + i] * ks[8 * s + i]);
+      beta = fmaf(ln.qv[8 * s + i], ks[128 + 8 * s + i], beta);
     }
-  } else if constexpr (!KTOK) {
-    h8_t bh[4], bl[4];
-    float beta = 0.f;
-    const float* ks = meta + 32 * ln.la;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float qt = ln.qv[8 * s + i] * ks[8 * s + i];
-        set_hi_lo(bh[s], bl[s], i, qt);
-        beta = fmaf(ln.qv[8 * s + i], ks[128 + 8 * s + i], beta);
-      }
-    }
-    beta = sum_lane_groups(beta);
+  return sum_lane_groups(beta);
+}
+
+// One 32-token group. KB/VB: code widths (16 = fp16 values, as in the tail).
+// bh/bl: the score B operand; beta: the key zero-point term (per-channel keys);
+// src: byte address of the lane whose scores this lane takes (per-channel keys
+// stacked over slots; < 0: its own); kmeta/vmeta: LDS copies of the group's meta.
+template <int KB, int VB, bool KTOK, int NS, bool TAIL>
+__device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t* vw, const float* kmeta,
+                                              const float* vmeta, int ntok, const h8_t* bh, const h8_t* bl,
+                                              float beta, int src, const Lane& ln, Acc& acc) {
+  float sc[8];  // token 16 t + 4 la + i at index 4 t + i
+  if constexpr (!KTOK || KB == 16) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f4_t c = {0.f, 0.f, 0.f, 0.f}, cl = {0.f, 0.f, 0.f, 0.f};
@@ -196,24 +198,31 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
         cl = mfma(A, bl[s], cl);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[t][i] = fmaf(fmaf(cl[i], kLoDown, c[i]), code_scale<KB>(), beta);
+      for (int i = 0; i < 4; ++i) sc[4 * t + i] = fmaf(fmaf(cl[i], kLoDown, c[i]), code_scale<KB>(), beta);
+    }
+    if constexpr (KB < 16) {
+      if (src >= 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[i] = bpermute(src, sc[i]);
+      }
     }
   } else {
     // per-token keys: one accumulator per 32-channel group n (= K-step)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int i = 0; i < 8; ++i) sc[i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[t][i] = 0.f;
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         f4_t c = {0.f, 0.f, 0.f, 0.f}, cl = {0.f, 0.f, 0.f, 0.f};
         const h8_t A = unpack8<KB>(kw, 4 * t + s);
-        c = mfma(A, qh[s], c);
-        cl = mfma(A, ql[s], cl);
-        const float* km = meta + 32 * s + 8 * ln.la + 4 * t;
+        c = mfma(A, bh[s], c);
+        cl = mfma(A, bl[s], cl);
+        const float* km = kmeta + 32 * s + 8 * ln.la + 4 * t;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          sc[t][i] = fmaf(fmaf(cl[i], kLoDown, c[i]) * code_scale<KB>(), km[i], fmaf(km[128 + i], ln.qn[s], sc[t][i]));
+          sc[4 * t + i] = fmaf(fmaf(cl[i], kLoDown, c[i]) * code_scale<KB>(), km[i],
+                               fmaf(km[128 + i], ln.qn[s], sc[4 * t + i]));
       }
     }
   }
@@ -222,11 +231,10 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (16 * t + 4 * ln.la + i >= ntok) sc[t][i] = -INFINITY;
+        if (16 * t + 4 * ln.la + i >= ntok) sc[4 * t + i] = -INFINITY;
   }
   // --------------------------------------------------------------- softmax
-  float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
   bm = max_lane_groups(bm);
   const float mnew = fmaxf(acc.m, bm);
   if (__any(mnew > acc.m)) {
@@ -243,13 +251,10 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
   }
   float p[8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(sc[t][i] - acc.m);
-      p[4 * t + i] = e;
-      acc.lpart += e;
-    }
+  for (int i = 0; i < 8; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(sc[i] - acc.m);
+    acc.lpart += p[i];
+  }
   // ------------------------------------------------------------ P . V
   u4_t vmask = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
   if constexpr (TAIL) {
@@ -260,44 +265,45 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
       vmask[q] = (j0 < ntok ? 0x0000FFFFu : 0u) | (j0 + 1 < ntok ? 0xFFFF0000u : 0u);
     }
   }
-  const int NP = 4 / ln.NS;
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    if (pass >= NP) continue;
-    const int n = ln.col_ok ? pass * ln.NS + ln.ns : 0;
-    h8_t bh, bl;
+  for (int pass = 0; pass < 4 / NS; ++pass) {
+    h8_t vh, vl;
     if constexpr (VB == 16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) set_hi_lo(bh, bl, i, p[i]);
+      for (int i = 0; i < 8; ++i) set_hi_lo(vh, vl, i, p[i]);
     } else {
-      const float* vs = meta + 256 + 32 * n + 8 * ln.la;
+      const int n = ln.col_ok ? pass * NS + ln.slot : 0;
+      const float* vs = vmeta + 32 * n + 8 * ln.la;
       float zp = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        set_hi_lo(bh, bl, i, p[i] * vs[i]);
+        set_hi_lo(vh, vl, i, p[i] * vs[i]);
         zp = fmaf(p[i], vs[128 + i], zp);
       }
       acc.zpart[pass] += zp;
     }
-    // M-tiles of channel groups pass*NS .. pass*NS + NS - 1 (two 16-channel tiles each)
+    // the two 16-channel tiles of each of channel groups pass*NS .. pass*NS + NS - 1
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u / 2 < pass * ln.NS || u / 2 >= (pass + 1) * ln.NS) continue;
+    for (int u = 2 * pass * NS; u < 2 * (pass + 1) * NS; ++u) {
       h8_t A = unpack8<VB>(vw, u);
       if constexpr (TAIL) {
         u4_t x = __builtin_bit_cast(u4_t, A);
         x &= vmask;
         A = __builtin_bit_cast(h8_t, x);
       }
-      acc.o[u] = mfma(A, bh, acc.o[u]);
-      acc.ol[u] = mfma(A, bl, acc.ol[u]);
+      acc.o[u] = mfma(A, vh, acc.o[u]);
+      acc.ol[u] = mfma(A, vl, acc.ol[u]);
     }
   }
 }
 
-template <int KB, int VB, bool KTOK>
-__global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
-  __shared__ float s_meta[kWaves][512];
+template <int KB, int VB, bool KTOK, int NS>
+__global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
+  constexpr bool STACK = KB < 16 && !KTOK;  // per-channel keys: one B operand for NS groups
+  constexpr int R = STACK ? NS : 1;
+  constexpr int NKW = 2 * KB, NVW = 2 * VB;
+  __shared__ float s_kmeta[kWaves][R][256];
+  __shared__ float s_vmeta[kWaves][256];
   __shared__ float s_o[kWaves][kMaxG][D];
   __shared__ float s_ml[kWaves][2][kMaxG];
   const LayerGeom& g = a.geo;
@@ -319,11 +325,10 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
   Lane ln;
   ln.lane = tid & 63;
   ln.la = ln.lane >> 4;
-  ln.c16 = ln.lane & 15;
-  ln.gcol = ln.c16 % G;
-  ln.NS = (16 / G >= 4) ? 4 : (16 / G >= 2 ? 2 : 1);  // channel groups per output pass (divides 4)
-  ln.ns = ln.c16 / G;
-  ln.col_ok = ln.ns < ln.NS;
+  const int c16 = ln.lane & 15;
+  ln.gcol = c16 % G;
+  ln.slot = c16 / G;
+  ln.col_ok = ln.slot < NS;
   {
     const uint16_t* qrow = a.q + ((size_t)r * g.hq + h * G + ln.gcol) * D;
 #pragma unroll
@@ -333,12 +338,14 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) ln.qv[8 * s + i] = (float)hv[i] * a.scale_log2;
     }
+    if constexpr (KTOK && KB < 16) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float part = 0.f;
+      for (int s = 0; s < 4; ++s) {
+        float part = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) part += ln.qv[8 * s + i];
-      ln.qn[s] = sum_lane_groups(part);
+        for (int i = 0; i < 8; ++i) part += ln.qv[8 * s + i];
+        ln.qn[s] = sum_lane_groups(part);
+      }
     }
   }
   Acc acc;
@@ -351,9 +358,10 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
   acc.lpart = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) acc.zpart[k] = 0.f;
-  float* meta = s_meta[wave];
+  float* kmeta = &s_kmeta[wave][0][0];
+  float* vmeta = s_vmeta[wave];
 
-  // the tail group first (true units), then the packed groups
+  // ------------------------------------ the tail group first, in true units
   const bool has_tail = T > 0 && nq >= g0 && nq < g1;
   if (has_tail && ((nq - g0) & (kWaves - 1)) == wave) {
     const uint8_t* rec = stream + g.tail_offset;
@@ -362,7 +370,7 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
     load_codes<16>(rec + 8192, ln.lane, vw);
     h8_t th[4], tl[4];
     q_operands(ln, th, tl);
-    process_group<16, 16, false, true>(kw, vw, meta, T, ln, th, tl, acc);
+    process_group<16, 16, false, NS, true>(kw, vw, kmeta, vmeta, T, th, tl, 0.f, -1, ln, acc);
     if constexpr (VB < 16) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {  // into the packed groups' units
@@ -371,40 +379,63 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
       }
     }
   }
+
+  // ----------------------------- the wave's packed groups: g0 + wave + 4 k
+  const int first = g0 + wave;
   const int qend = min(g1, nq);
-  int vg = g0 + wave;
-  if (vg < qend) {
-    constexpr int NKW = 2 * KB, NVW = 2 * VB;
+  const int nk = first < qend ? (qend - first + kWaves - 1) / kWaves : 0;
+  if (nk > 0) {
     const uint32_t rb = (uint32_t)g.record_bytes;
     const RecordParts parts = record_parts(KB, VB);
+    auto rec_of = [&](int k) { return stream + (size_t)(first + kWaves * k) * rb; };
     uint32_t kw[NKW], vw[NVW];
-    u4_t km = {0, 0, 0, 0}, vm = {0, 0, 0, 0};
-    h8_t mh[4], ml[4];
-    if constexpr (KB == 16 || KTOK) q_operands(ln, mh, ml);
-    const uint8_t* rec = stream + (size_t)vg * rb;
-    load_codes<KB>(rec, ln.lane, kw);
-    load_codes<VB>(rec + parts.vcode, ln.lane, vw);
-    if constexpr (KB < 16) km = *(const u4_t*)(rec + parts.kmeta + ln.lane * 16);
-    if constexpr (VB < 16) vm = *(const u4_t*)(rec + parts.vmeta + ln.lane * 16);
-    for (; vg < qend; vg += kWaves) {
-      // meta of this group into the wave's LDS slot
-      if constexpr (KB < 16) *(u4_t*)(meta + 4 * ln.lane) = km;
-      if constexpr (VB < 16) *(u4_t*)(meta + 256 + 4 * ln.lane) = vm;
+    u4_t kmr[R], vm = {0, 0, 0, 0};
+    h8_t bh[4], bl[4];
+    float beta = 0.f;
+    if constexpr (!STACK) q_operands(ln, bh, bl);
+    load_codes<KB>(rec_of(0), ln.lane, kw);
+    load_codes<VB>(rec_of(0) + parts.vcode, ln.lane, vw);
+    if constexpr (VB < 16) vm = *(const u4_t*)(rec_of(0) + parts.vmeta + ln.lane * 16);
+    if constexpr (KB < 16) {
+#pragma unroll
+      for (int e = 0; e < R; ++e)
+        kmr[e] = e < nk ? *(const u4_t*)(rec_of(e) + parts.kmeta + ln.lane * 16) : u4_t{0, 0, 0, 0};
+    }
+    for (int k = 0; k < nk; ++k) {
+      const int e = STACK ? k % R : 0;  // slot of this group in its stack
+      if constexpr (KB < 16) {
+        if (e == 0) {
+#pragma unroll
+          for (int f = 0; f < R; ++f) *(u4_t*)(kmeta + 256 * f + 4 * ln.lane) = kmr[f];
+        }
+      }
+      if constexpr (VB < 16) *(u4_t*)(vmeta + 4 * ln.lane) = vm;
       wave_sync_lds();
       uint32_t kc[NKW], vc[NVW];
 #pragma unroll
       for (int i = 0; i < NKW; ++i) kc[i] = kw[i];
 #pragma unroll
       for (int i = 0; i < NVW; ++i) vc[i] = vw[i];
-      const int nx = vg + kWaves;
-      if (nx < qend) {  // prefetch the wave's next group
-        const uint8_t* nrec = stream + (size_t)nx * rb;
+      if (k + 1 < nk) {  // the next group's loads go out before this group's math
+        const uint8_t* nrec = rec_of(k + 1);
         load_codes<KB>(nrec, ln.lane, kw);
         load_codes<VB>(nrec + parts.vcode, ln.lane, vw);
-        if constexpr (KB < 16) km = *(const u4_t*)(nrec + parts.kmeta + ln.lane * 16);
         if constexpr (VB < 16) vm = *(const u4_t*)(nrec + parts.vmeta + ln.lane * 16);
+        if constexpr (KB < 16) {
+          if (!STACK || (k + 1) % R == 0) {
+#pragma unroll
+            for (int f = 0; f < R; ++f)
+              kmr[f] = k + 1 + f < nk ? *(const u4_t*)(rec_of(k + 1 + f) + parts.kmeta + ln.lane * 16)
+                                      : u4_t{0, 0, 0, 0};
+          }
+        }
       }
-      process_group<KB, VB, KTOK, false>(kc, vc, meta, GS, ln, mh, ml, acc);
+      int src = -1;
+      if constexpr (STACK) {
+        if (e == 0) beta = k_operands(ln, kmeta + 256 * (ln.col_ok ? ln.slot : 0), bh, bl);
+        src = ((ln.lane & 48) | (ln.gcol + G * e)) * 4;
+      }
+      process_group<KB, VB, KTOK, NS, false>(kc, vc, kmeta, vmeta, GS, bh, bl, beta, src, ln, acc);
       wave_sync_lds();
     }
   }
@@ -412,15 +443,13 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
   // ------------------------------------------- this wave's result into LDS
   const float l = sum_lane_groups(acc.lpart);
   const float vmul = code_scale<VB>();
-  const int NP = 4 / ln.NS;
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    if (pass >= NP) continue;
+  for (int pass = 0; pass < 4 / NS; ++pass) {
     const float z = sum_lane_groups(acc.zpart[pass]);
-    const int n = pass * ln.NS + ln.ns;
+    const int n = pass * NS + ln.slot;
     if (ln.col_ok) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 2 * pass * NS; u < 2 * (pass + 1) * NS; ++u) {
         if (u / 2 != n) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -433,7 +462,7 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
     s_ml[wave][1][ln.lane] = l;
   }
   __syncthreads();
-  // ------------------------------------ combine the four waves, write partial
+  // ------------------------------------ combine the four waves and write
   for (int idx = tid; idx < G * D; idx += blockDim.x) {
     const int gg = idx >> 7, c = idx & 127;
     float M = -INFINITY;
@@ -450,17 +479,38 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(DecodeArgs a) {
         den = fmaf(e, s_ml[w][1][gg], den);
       }
     }
-    const size_t row = ((size_t)r * g.hq + h * G + gg) * a.splits + split;
-    a.part_o[row * D + c] = den > 0.f ? num / den : 0.f;
-    if (c == 0) a.part_lse[row] = den > 0.f ? (M + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    const float o = den > 0.f ? num / den : 0.f;
+    const float lse = den > 0.f ? (M + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    const size_t qrow = (size_t)r * g.hq + h * G + gg;
+    if (a.splits == 1) {  // the only split: final output
+      if (a.out_f32)
+        ((float*)a.out)[qrow * D + c] = o;
+      else
+        ((_Float16*)a.out)[qrow * D + c] = (_Float16)o;
+      if (c == 0 && a.lse_out) a.lse_out[qrow] = lse;
+    } else {
+      const size_t row = qrow * a.splits + split;
+      a.part_o[row * D + c] = o;
+      if (c == 0) a.part_lse[row] = lse;
+    }
   }
+}
+
+template <int KB, int VB, int NS>
+hipError_t launch_kvn(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
+  const dim3 grid(a.splits, a.geo.hkv, batch), block(256);
+  if constexpr (KB < 16) {
+    if (a.geo.k_token) return launch_timed(split_mfma_kernel<KB, VB, true, NS>, grid, block, s, ev, a);
+  }
+  return launch_timed(split_mfma_kernel<KB, VB, false, NS>, grid, block, s, ev, a);
 }
 
 template <int KB, int VB>
 hipError_t launch_kv(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
-  const dim3 grid(a.splits, a.geo.hkv, batch), block(256);
-  if (a.geo.k_token && KB < 16) return launch_timed(split_mfma_kernel<KB, VB, true>, grid, block, s, ev, a);
-  return launch_timed(split_mfma_kernel<KB, VB, false>, grid, block, s, ev, a);
+  const int per = 16 / a.geo.g;
+  if (per >= 4) return launch_kvn<KB, VB, 4>(a, batch, s, ev);
+  if (per >= 2) return launch_kvn<KB, VB, 2>(a, batch, s, ev);
+  return launch_kvn<KB, VB, 1>(a, batch, s, ev);
 }
 
 template <int KB>
