@@ -145,8 +145,8 @@ __device__ inline float bpermute(int addr, float v) {
 struct Lane {
   int lane, la, gcol, slot;
   bool col_ok;
-  float qv[32];  // q' of the lane's row for channels 32 s + 8 la + i, index 8 s + i
-  float qn[4];   // per 32-channel group sums of q' (per-token keys)
+  const float* qv;  // LDS: q' of the lane's row at channels 32 s + 8 la + i is qv[32 s + i]
+  float qn[4];      // per 32-channel group sums of q' (per-token keys)
 };
 
 struct Acc {
@@ -160,7 +160,7 @@ __device__ inline void q_operands(const Lane& ln, h8_t* qh, h8_t* ql) {
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) set_hi_lo(qh[s], ql[s], i, ln.qv[8 * s + i]);
+    for (int i = 0; i < 8; ++i) set_hi_lo(qh[s], ql[s], i, ln.qv[32 * s + i]);
 }
 
 // B operand q' * scale_k of per-channel keys for the group of this lane's slot,
@@ -172,8 +172,9 @@ __device__ inline float k_operands(const Lane& ln, const float* kmeta, h8_t* bh,
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      set_hi_lo(bh[s], bl[s], i, ln.qv[8 * s + i] * ks[8 * s + i]);
-      beta = fmaf(ln.qv[8 * s + i], ks[128 + 8 * s + i], beta);
+      const float q = ln.qv[32 * s + i];
+      set_hi_lo(bh[s], bl[s], i, q * ks[8 * s + i]);
+      beta = fmaf(q, ks[128 + 8 * s + i], beta);
     }
   return sum_lane_groups(beta);
 }
@@ -306,6 +307,7 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   __shared__ float s_vmeta[kWaves][256];
   __shared__ float s_o[kWaves][kMaxG][D];
   __shared__ float s_ml[kWaves][2][kMaxG];
+  __shared__ float s_q[kMaxG][D];
   const LayerGeom& g = a.geo;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -329,23 +331,18 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   ln.gcol = c16 % G;
   ln.slot = c16 / G;
   ln.col_ok = ln.slot < NS;
-  {
-    const uint16_t* qrow = a.q + ((size_t)r * g.hq + h * G + ln.gcol) * D;
+  for (int idx = tid; idx < G * D; idx += blockDim.x)
+    s_q[idx >> 7][idx & 127] = (float)__builtin_bit_cast(_Float16, a.q[((size_t)r * g.hq + h * G) * D + idx]) *
+                               a.scale_log2;
+  __syncthreads();
+  ln.qv = &s_q[ln.gcol][8 * ln.la];
+  if constexpr (KTOK && KB < 16) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const u4_t v = *(const u4_t*)(qrow + 32 * s + 8 * ln.la);
-      const h8_t hv = __builtin_bit_cast(h8_t, v);
+      float part = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ln.qv[8 * s + i] = (float)hv[i] * a.scale_log2;
-    }
-    if constexpr (KTOK && KB < 16) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) part += ln.qv[8 * s + i];
-        ln.qn[s] = sum_lane_groups(part);
-      }
+      for (int i = 0; i < 8; ++i) part += ln.qv[32 * s + i];
+      ln.qn[s] = sum_lane_groups(part);
     }
   }
   Acc acc;
