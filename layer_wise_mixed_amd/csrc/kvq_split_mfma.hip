@@ -34,6 +34,8 @@
 // land in exactly the registers the P.V tile needs as its reduction index.
 // The fp16 tail (tokens that do not fill a group) is processed first, in true
 // units, by the wave that owns it, with invalid token slots masked.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -179,15 +181,15 @@ __device__ inline float k_operands(const Lane& ln, const float* kmeta, h8_t* bh,
   return sum_lane_groups(beta);
 }
 
-// One 32-token group. KB/VB: code widths (16 = fp16 values, as in the tail).
-// bh/bl: the score B operand; beta: the key zero-point term (per-channel keys);
-// src: byte address of the lane whose scores this lane takes (per-channel keys
-// stacked over slots; < 0: its own); kmeta/vmeta: LDS copies of the group's meta.
-template <int KB, int VB, bool KTOK, int NS, bool TAIL>
-__device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t* vw, const float* kmeta,
-                                              const float* vmeta, int ntok, const h8_t* bh, const h8_t* bl,
-                                              float beta, int src, const Lane& ln, Acc& acc) {
-  float sc[8];  // token 16 t + 4 la + i at index 4 t + i
+// Scores of one 32-token group in log2 units, token 16 t + 4 la + i at index
+// 4 t + i. KB: key code width (16 = fp16 values, as in the tail); bh/bl: the
+// score B operand; beta: the key zero-point term (per-channel keys); src: byte
+// address of the lane whose scores this lane takes (per-channel keys stacked
+// over slots; < 0: its own); kmeta: LDS copy of the group's key meta
+// (per-token keys). Tail slots at or past ntok get -inf.
+template <int KB, bool KTOK, bool TAIL>
+__device__ __forceinline__ void group_scores(const uint32_t* kw, const float* kmeta, int ntok, const h8_t* bh,
+                                             const h8_t* bl, float beta, int src, const Lane& ln, float* sc) {
   if constexpr (!KTOK || KB == 16) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -234,8 +236,10 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
       for (int i = 0; i < 4; ++i)
         if (16 * t + 4 * ln.la + i >= ntok) sc[4 * t + i] = -INFINITY;
   }
-  // --------------------------------------------------------------- softmax
-  float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+}
+
+// Raise the running max to cover a block max; rescale what was accumulated.
+__device__ __forceinline__ void raise_max(float bm, Acc& acc) {
   bm = max_lane_groups(bm);
   const float mnew = fmaxf(acc.m, bm);
   if (__any(mnew > acc.m)) {
@@ -250,13 +254,19 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
     for (int k = 0; k < 4; ++k) acc.zpart[k] *= alpha;
     acc.m = mnew;
   }
+}
+
+// p = exp2(score - max) of one group, and its P.V products. VB: value code
+// width; vmeta: LDS copy of the group's value meta.
+template <int VB, int NS, bool TAIL>
+__device__ __forceinline__ void group_pv(const uint32_t* vw, const float* vmeta, int ntok, const float* sc,
+                                         const Lane& ln, Acc& acc) {
   float p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     p[i] = __builtin_amdgcn_exp2f(sc[i] - acc.m);
     acc.lpart += p[i];
   }
-  // ------------------------------------------------------------ P . V
   u4_t vmask = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
   if constexpr (TAIL) {
     // reduction index i' of this lane holds token 16 (i'/4) + 4 la + i' % 4
@@ -298,19 +308,31 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
   }
 }
 
+template <int KB, int VB, bool KTOK, int NS, bool TAIL>
+__device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t* vw, const float* kmeta,
+                                              const float* vmeta, int ntok, const h8_t* bh, const h8_t* bl,
+                                              float beta, int src, const Lane& ln, Acc& acc) {
+  float sc[8];
+  group_scores<KB, KTOK, TAIL>(kw, kmeta, ntok, bh, bl, beta, src, ln, sc);
+  raise_max(fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))),
+            acc);
+  group_pv<VB, NS, TAIL>(vw, vmeta, ntok, sc, ln, acc);
+}
+
 template <int KB, int VB, bool KTOK, int NS>
 __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   constexpr bool STACK = KB < 16 && !KTOK;  // per-channel keys: one B operand for NS groups
   constexpr int R = STACK ? NS : 1;
   constexpr int NKW = 2 * KB, NVW = 2 * VB;
-  __shared__ float s_kmeta[kWaves][R][256];
+  constexpr int KM = R;  // key meta records staged per refresh
+  __shared__ float s_kmeta[kWaves][KM][256];
   __shared__ float s_vmeta[kWaves][256];
   __shared__ float s_o[kWaves][kMaxG][D];
   __shared__ float s_ml[kWaves][2][kMaxG];
   __shared__ float s_q[kMaxG][D];
   const LayerGeom& g = a.geo;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int G = g.g;
   int L = a.seq_lens[r];
@@ -378,53 +400,54 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   }
 
   // ----------------------------- the wave's packed groups: g0 + wave + 4 k
+  // Each loop is unrolled by its two register buffers so that every buffer
+  // index is static (no register copies).
   const int first = g0 + wave;
   const int qend = min(g1, nq);
   const int nk = first < qend ? (qend - first + kWaves - 1) / kWaves : 0;
+  const uint32_t rb = (uint32_t)g.record_bytes;
+  const RecordParts parts = record_parts(KB, VB);
+  auto rec_of = [&](int k) { return stream + (size_t)(first + kWaves * k) * rb; };
+  auto kmeta_of = [&](int k) { return *(const u4_t*)(rec_of(k) + parts.kmeta + ln.lane * 16); };
   if (nk > 0) {
-    const uint32_t rb = (uint32_t)g.record_bytes;
-    const RecordParts parts = record_parts(KB, VB);
-    auto rec_of = [&](int k) { return stream + (size_t)(first + kWaves * k) * rb; };
-    uint32_t kw[NKW], vw[NVW];
-    u4_t kmr[R], vm = {0, 0, 0, 0};
+    // One group at a time, one group loading ahead.
+    struct Buf {
+      uint32_t kw[NKW];
+      uint32_t vw[NVW];
+      u4_t vm;
+    };
+    Buf buf[2];
+    u4_t kmr[KM];
     h8_t bh[4], bl[4];
     float beta = 0.f;
     if constexpr (!STACK) q_operands(ln, bh, bl);
-    load_codes<KB>(rec_of(0), ln.lane, kw);
-    load_codes<VB>(rec_of(0) + parts.vcode, ln.lane, vw);
-    if constexpr (VB < 16) vm = *(const u4_t*)(rec_of(0) + parts.vmeta + ln.lane * 16);
+    auto issue = [&](Buf& bf, int k) {
+      const uint8_t* rec = rec_of(k);
+      load_codes<KB>(rec, ln.lane, bf.kw);
+      load_codes<VB>(rec + parts.vcode, ln.lane, bf.vw);
+      if constexpr (VB < 16) bf.vm = *(const u4_t*)(rec + parts.vmeta + ln.lane * 16);
+    };
+    issue(buf[0], 0);
     if constexpr (KB < 16) {
 #pragma unroll
-      for (int e = 0; e < R; ++e)
-        kmr[e] = e < nk ? *(const u4_t*)(rec_of(e) + parts.kmeta + ln.lane * 16) : u4_t{0, 0, 0, 0};
+      for (int f = 0; f < KM; ++f) kmr[f] = f < nk ? kmeta_of(f) : u4_t{0, 0, 0, 0};
     }
-    for (int k = 0; k < nk; ++k) {
+    auto step = [&](auto J, int k) {
+      constexpr int j = decltype(J)::value;
       const int e = STACK ? k % R : 0;  // slot of this group in its stack
       if constexpr (KB < 16) {
         if (e == 0) {
 #pragma unroll
-          for (int f = 0; f < R; ++f) *(u4_t*)(kmeta + 256 * f + 4 * ln.lane) = kmr[f];
+          for (int f = 0; f < KM; ++f) *(u4_t*)(kmeta + 256 * f + 4 * ln.lane) = kmr[f];
         }
       }
-      if constexpr (VB < 16) *(u4_t*)(vmeta + 4 * ln.lane) = vm;
+      if constexpr (VB < 16) *(u4_t*)(vmeta + 4 * ln.lane) = buf[j].vm;
       wave_sync_lds();
-      uint32_t kc[NKW], vc[NVW];
+      if (k + 1 < nk) issue(buf[j ^ 1], k + 1);
+      if constexpr (KB < 16) {
+        if (k + 1 < nk && (k + 1) % KM == 0) {
 #pragma unroll
-      for (int i = 0; i < NKW; ++i) kc[i] = kw[i];
-#pragma unroll
-      for (int i = 0; i < NVW; ++i) vc[i] = vw[i];
-      if (k + 1 < nk) {  // the next group's loads go out before this group's math
-        const uint8_t* nrec = rec_of(k + 1);
-        load_codes<KB>(nrec, ln.lane, kw);
-        load_codes<VB>(nrec + parts.vcode, ln.lane, vw);
-        if constexpr (VB < 16) vm = *(const u4_t*)(nrec + parts.vmeta + ln.lane * 16);
-        if constexpr (KB < 16) {
-          if (!STACK || (k + 1) % R == 0) {
-#pragma unroll
-            for (int f = 0; f < R; ++f)
-              kmr[f] = k + 1 + f < nk ? *(const u4_t*)(rec_of(k + 1 + f) + parts.kmeta + ln.lane * 16)
-                                      : u4_t{0, 0, 0, 0};
-          }
+          for (int f = 0; f < KM; ++f) kmr[f] = k + 1 + f < nk ? kmeta_of(k + 1 + f) : u4_t{0, 0, 0, 0};
         }
       }
       int src = -1;
@@ -432,8 +455,12 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
         if (e == 0) beta = k_operands(ln, kmeta + 256 * (ln.col_ok ? ln.slot : 0), bh, bl);
         src = ((ln.lane & 48) | (ln.gcol + G * e)) * 4;
       }
-      process_group<KB, VB, KTOK, NS, false>(kc, vc, kmeta, vmeta, GS, bh, bl, beta, src, ln, acc);
+      process_group<KB, VB, KTOK, NS, false>(buf[j].kw, buf[j].vw, kmeta, vmeta, GS, bh, bl, beta, src, ln, acc);
       wave_sync_lds();
+    };
+    for (int k = 0; k < nk; k += 2) {
+      step(std::integral_constant<int, 0>{}, k);
+      if (k + 1 < nk) step(std::integral_constant<int, 1>{}, k + 1);
     }
   }
 
