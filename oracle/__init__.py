@@ -17,6 +17,10 @@ Functions and the passages they follow:
   lse_merge           -- split merge by log-sum-exp (TriAxialKV page,
                          "Facts": split decode bullet)
   pack_stream / unpack_stream -- this project's byte layout of the cache
+  quantize_tokens / pack_paged / unpack_paged / decode_paged -- the paged
+                         INT2/INT4 pool (TriAxialKV page, "Facts": page-pool,
+                         leftover-routing and page-table bullets; INT4 keys
+                         and values per-token)
   equiv_bits          -- mean over layers of (bK + bV) / 2 (KVTuner summary
                          page, "Experimental setup": equivalent precision;
                          first page, "Facts": K8V2 is called 5-bit, K4V8 6-bit)
@@ -90,6 +94,20 @@ def lib():
         L.oq_meta_channel_index.restype = i32
         L.oq_meta_token_index.argtypes = [i32, i32]
         L.oq_meta_token_index.restype = i32
+        for name in ("oq_page_k_site", "oq_page_v_site"):
+            getattr(L, name).argtypes = [i32, i32, P, P]
+            getattr(L, name).restype = None
+        L.oq_page_meta_index.argtypes = [i32, i32]
+        L.oq_page_meta_index.restype = i32
+        L.oq_quantize_tokens.argtypes = [P, i64, i32, P, P, P]
+        L.oq_quantize_tokens.restype = None
+        L.oq_pack_paged.argtypes = [P, P, i64, i64, P, ctypes.c_int32, i32, i32, P, P]
+        L.oq_pack_paged.restype = None
+        L.oq_unpack_paged.argtypes = [P, i64, i64, P, ctypes.c_int32, i32, i32, P, P]
+        L.oq_unpack_paged.restype = None
+        L.oq_decode_paged.argtypes = [P, i32, P, P, P, P, P, i64, ctypes.c_int32, i32, P, i32,
+                                      ctypes.c_double, P, P, i32]
+        L.oq_decode_paged.restype = i32
         _lib = L
     return _lib
 
@@ -216,6 +234,82 @@ def meta_channel_index(c: int) -> int:
 
 def meta_token_index(j: int, n: int) -> int:
     return int(lib().oq_meta_token_index(j, n))
+
+
+# ----------------------------------------------------------------- paged pool
+
+PAGE_TOKENS = 16
+
+
+def page_k_site(p: int, c: int):
+    """(byte, shift) of key (slot p, channel c) inside one KV head's INT4 page."""
+    b, sh = ctypes.c_int(), ctypes.c_int()
+    lib().oq_page_k_site(p, c, ctypes.byref(b), ctypes.byref(sh))
+    return b.value, sh.value
+
+
+def page_v_site(p: int, c: int):
+    b, sh = ctypes.c_int(), ctypes.c_int()
+    lib().oq_page_v_site(p, c, ctypes.byref(b), ctypes.byref(sh))
+    return b.value, sh.value
+
+
+def page_meta_index(p: int, n: int) -> int:
+    return int(lib().oq_page_meta_index(p, n))
+
+
+def quantize_tokens(x_fp16, bits: int):
+    """Per-token quantization (four 32-channel groups per token) of fp16 [L, 128]:
+    (codes [L, 128] uint8, scale [L, 4], zero [L, 4])."""
+    x = _u16(x_fp16).reshape(-1, D)
+    L = x.shape[0]
+    codes = np.zeros((L, D), np.uint8)
+    sc = np.zeros((max(L, 1), 4), np.float32)
+    zr = np.zeros((max(L, 1), 4), np.float32)
+    lib().oq_quantize_tokens(_p(x), L, bits, _p(codes), _p(sc), _p(zr))
+    return codes, sc[:L], zr[:L]
+
+
+def paged_pool_bytes(hkv: int, int2_pages: int, int4_pages: int) -> int:
+    return int2_pages * hkv * 2048 + int4_pages * hkv * 3072
+
+
+def pack_paged(pool: np.ndarray, k_fp16, v_fp16, n2: int, table, int2_pages: int, hkv: int, h: int,
+               mask: np.ndarray | None = None):
+    """Quantize one (request, KV head) -- fp16 [n2 + n4, 128] in logical order, INT2 tokens
+    first -- into `pool` (uint8, modified in place) through its page table."""
+    k = _u16(k_fp16).reshape(-1, D)
+    v = _u16(v_fp16).reshape(-1, D)
+    assert n2 % GROUP == 0 and 0 <= n2 <= k.shape[0]
+    tb = np.ascontiguousarray(table, dtype=np.int32)
+    lib().oq_pack_paged(_p(k), _p(v), n2, k.shape[0] - n2, _p(tb), int2_pages, hkv, h, _p(pool),
+                        _p(mask) if mask is not None else None)
+
+
+def unpack_paged(pool: np.ndarray, n2: int, n4: int, table, int2_pages: int, hkv: int, h: int):
+    """float32 (kdeq, vdeq) [n2 + n4, 128] of one (request, KV head), logical order."""
+    tb = np.ascontiguousarray(table, dtype=np.int32)
+    kd = np.zeros((n2 + n4, D), np.float32)
+    vd = np.zeros((n2 + n4, D), np.float32)
+    lib().oq_unpack_paged(_p(pool), n2, n4, _p(tb), int2_pages, hkv, h, _p(kd), _p(vd))
+    return kd, vd
+
+
+def decode_paged(pool: np.ndarray, req, head, n2, n4, tables: np.ndarray, int2_pages: int, hkv: int,
+                 q_fp16, G: int, scale: float, nthreads: int = 0):
+    """One decode step over the oracle's own paged pool: (out, lse, threads)."""
+    req = np.ascontiguousarray(req, dtype=np.int64)
+    head = np.ascontiguousarray(head, dtype=np.int64)
+    n2 = np.ascontiguousarray(n2, dtype=np.int64)
+    n4 = np.ascontiguousarray(n4, dtype=np.int64)
+    tb = np.ascontiguousarray(tables, dtype=np.int32)
+    ns = len(req)
+    q = _u16(q_fp16).reshape(ns, G, D)
+    out = np.zeros((ns, G, D), np.float64)
+    lse = np.zeros((ns, G), np.float64)
+    used = lib().oq_decode_paged(_p(pool), ns, _p(req), _p(head), _p(n2), _p(n4), _p(tb), tb.shape[1],
+                                 int2_pages, hkv, _p(q), G, float(scale), _p(out), _p(lse), nthreads)
+    return out, lse, used
 
 
 # ------------------------------------------------------------------ attention

@@ -379,6 +379,165 @@ void oq_unpack_stream(const uint8_t *bytes, int64_t L, int kb, int vb, int kaxis
     }
 }
 
+/* ---------------------------------------------------------- paged pool -- */
+/*
+ * The paged pool of one layer (TriAxialKV page, "Facts": INT2 and INT4 page
+ * pools share one address space split at an offset; INT2 keys per-channel
+ * and values per-token, INT4 keys and values per-token; INT2 tokens that do
+ * not fill a 32-token group go to the INT4 per-token path; each request's
+ * page table lists its INT2 pages before its INT4 pages). A page holds 16
+ * tokens of every KV head. Page ids below int2_pages are INT2 pages, the
+ * rest INT4 pages.
+ *  - INT2 region at byte 0, int2_page_bytes = hkv * 2048 per page. A 32-token
+ *    group needs an aligned pair of pages (P even, P + 1): the pair holds one
+ *    K2V2 group record (layout above, keys per-channel) per KV head, head h
+ *    at P * int2_page_bytes + h * 4096.
+ *  - INT4 region at int4_offset = int2_pages * int2_page_bytes,
+ *    int4_page_bytes = hkv * 3072 per page; page P, head h at
+ *    int4_offset + (P - int2_pages) * int4_page_bytes + h * 3072:
+ *      [K codes 1024 B][V codes 1024 B][K meta 512 B][V meta 512 B]
+ *    for token slots p = 0..15, 4-bit codes, lane word w at lane * 16 + w * 4:
+ *      K (p, c): lane 16*((c/8)%4) + p, word c/32, position c%8 of the word
+ *                (even positions in bits 0..15, odd in 16..31, 4 bits each)
+ *      V (p, c): lane 16*(p/4) + c%16, word (c/16)/2,
+ *                bit 8*((c/16)%2) + 4*((p%4)/2) + 16*(p%2)
+ *      meta: 64 fp32 scales then 64 fp32 zeros, index 16*(c/32) + p.
+ * A request's table holds n2/16 INT2 entries (entry 2i = the even id of
+ * the pair of INT2 group i; entry 2i+1 = that id + 1) then ceil(n4/16) INT4
+ * entries (entry n2/16 + t/16 holds INT4 token t in slot t % 16). Its
+ * logical token list is the n2 INT2 tokens, then the n4 INT4 tokens.
+ */
+
+void oq_page_k_site(int p, int c, int *byte, int *shift)
+{
+    int lane = 16 * ((c / 8) % 4) + p;
+    int pos = c % 8;
+    *byte = lane * 16 + (c / 32) * 4;
+    *shift = 16 * (pos % 2) + 4 * (pos / 2);
+}
+
+void oq_page_v_site(int p, int c, int *byte, int *shift)
+{
+    int lane = 16 * (p / 4) + c % 16;
+    int u = c / 16;
+    *byte = 1024 + lane * 16 + (u / 2) * 4;
+    *shift = 8 * (u % 2) + 4 * ((p % 4) / 2) + 16 * (p % 2);
+}
+
+int oq_page_meta_index(int p, int n) { return 16 * n + p; }
+
+static void oq_put4(uint8_t *page, int byte, int shift, uint32_t code, uint8_t *mask)
+{
+    uint32_t w;
+    memcpy(&w, page + byte, 4);
+    w = (w & ~(0xFu << shift)) | ((code & 0xFu) << shift);
+    memcpy(page + byte, &w, 4);
+    if (mask) mask[byte + shift / 8] = 1;
+}
+
+static uint32_t oq_get4(const uint8_t *page, int byte, int shift)
+{
+    uint32_t w;
+    memcpy(&w, page + byte, 4);
+    return (w >> shift) & 0xFu;
+}
+
+/* Per-token quantization of L tokens (any L), each token in four 32-channel
+ * groups: code [L][128], scale/zero [L][4]. */
+void oq_quantize_tokens(const uint16_t *x, int64_t L, int bits, uint8_t *code, float *scale,
+                        float *zero)
+{
+    for (int64_t j = 0; j < L; ++j)
+        for (int n = 0; n < OQ_D / OQ_G; ++n)
+            oq_quantize_group(x + j * OQ_D + n * OQ_G, 1, OQ_G, bits, &scale[j * 4 + n],
+                              &zero[j * 4 + n], code + j * OQ_D + n * OQ_G);
+}
+
+static int64_t oq_int2_record_at(int32_t pair_page, int hkv, int h)
+{
+    return (int64_t)pair_page * hkv * 2048 + (int64_t)h * 4096;
+}
+
+static int64_t oq_int4_page_at(int32_t page, int32_t int2_pages, int hkv, int h)
+{
+    return (int64_t)int2_pages * hkv * 2048 + (int64_t)(page - int2_pages) * hkv * 3072 +
+           (int64_t)h * 3072;
+}
+
+/*
+ * Quantize and place the tokens of one (request, KV head) into the pool:
+ * k, v fp16 [n2 + n4][128] in logical order (n2 a multiple of 32). mask, if
+ * not NULL, gets 1 on every byte the call defines.
+ */
+void oq_pack_paged(const uint16_t *k, const uint16_t *v, int64_t n2, int64_t n4,
+                   const int32_t *table, int32_t int2_pages, int hkv, int h, uint8_t *pool,
+                   uint8_t *mask)
+{
+    /* INT2 groups: the K2V2 per-channel record of a 32-token group */
+    uint8_t kc[OQ_G * OQ_D], vc[OQ_G * OQ_D];
+    float ks[OQ_D], kz[OQ_D], vs[OQ_G * 4], vz[OQ_G * 4];
+    for (int64_t m = 0; m < n2 / OQ_G; ++m) {
+        const uint16_t *kg = k + m * OQ_G * OQ_D, *vg = v + m * OQ_G * OQ_D;
+        oq_quantize_stream(kg, vg, OQ_G, 2, 2, 0, kc, ks, kz, vc, vs, vz);
+        int64_t at = oq_int2_record_at(table[2 * m], hkv, h);
+        oq_pack_stream(kg, vg, OQ_G, 2, 2, 0, 0, kc, ks, kz, vc, vs, vz, pool + at,
+                       mask ? mask + at : NULL);
+    }
+    /* INT4 tokens: per-token keys and values, one page slot each */
+    uint8_t ck[OQ_D], cv[OQ_D];
+    float sk[4], zk[4], sv[4], zv[4];
+    for (int64_t t = 0; t < n4; ++t) {
+        const uint16_t *kt = k + (n2 + t) * OQ_D, *vt = v + (n2 + t) * OQ_D;
+        oq_quantize_tokens(kt, 1, 4, ck, sk, zk);
+        oq_quantize_tokens(vt, 1, 4, cv, sv, zv);
+        int64_t at = oq_int4_page_at(table[n2 / 16 + t / 16], int2_pages, hkv, h);
+        uint8_t *page = pool + at;
+        uint8_t *pm = mask ? mask + at : NULL;
+        int p = (int)(t % 16);
+        for (int c = 0; c < OQ_D; ++c) {
+            int b, sh;
+            oq_page_k_site(p, c, &b, &sh);
+            oq_put4(page, b, sh, ck[c], pm);
+            oq_page_v_site(p, c, &b, &sh);
+            oq_put4(page, b, sh, cv[c], pm);
+        }
+        for (int n = 0; n < 4; ++n) {
+            int ix = oq_page_meta_index(p, n);
+            oq_put_f32(page + 2048, ix, sk[n], pm ? pm + 2048 : NULL);
+            oq_put_f32(page + 2048, 64 + ix, zk[n], pm ? pm + 2048 : NULL);
+            oq_put_f32(page + 2560, ix, sv[n], pm ? pm + 2560 : NULL);
+            oq_put_f32(page + 2560, 64 + ix, zv[n], pm ? pm + 2560 : NULL);
+        }
+    }
+}
+
+/* Read one (request, KV head) back from the pool, dequantized, float
+ * [n2 + n4][128] each, in logical order. */
+void oq_unpack_paged(const uint8_t *pool, int64_t n2, int64_t n4, const int32_t *table,
+                     int32_t int2_pages, int hkv, int h, float *kdeq, float *vdeq)
+{
+    for (int64_t m = 0; m < n2 / OQ_G; ++m)
+        oq_unpack_stream(pool + oq_int2_record_at(table[2 * m], hkv, h), OQ_G, 2, 2, 0, 1,
+                         kdeq + m * OQ_G * OQ_D, vdeq + m * OQ_G * OQ_D);
+    for (int64_t t = 0; t < n4; ++t) {
+        const uint8_t *page = pool + oq_int4_page_at(table[n2 / 16 + t / 16], int2_pages, hkv, h);
+        int p = (int)(t % 16);
+        float *ko = kdeq + (n2 + t) * OQ_D, *vo = vdeq + (n2 + t) * OQ_D;
+        for (int c = 0; c < OQ_D; ++c) {
+            int b, sh, ix = oq_page_meta_index(p, c / OQ_G);
+            float s, z;
+            oq_page_k_site(p, c, &b, &sh);
+            memcpy(&s, page + 2048 + 4 * ix, 4);
+            memcpy(&z, page + 2048 + 4 * (64 + ix), 4);
+            ko[c] = oq_dequant(oq_get4(page, b, sh), s, z);
+            oq_page_v_site(p, c, &b, &sh);
+            memcpy(&s, page + 2560 + 4 * ix, 4);
+            memcpy(&z, page + 2560 + 4 * (64 + ix), 4);
+            vo[c] = oq_dequant(oq_get4(page, b, sh), s, z);
+        }
+    }
+}
+
 /* ----------------------------------------------------------- attention -- */
 
 /*
@@ -475,6 +634,42 @@ int oq_decode_packed(const uint8_t *cache, int64_t stream_stride, int n_streams,
         float *vd = (float *)malloc(sizeof(float) * (size_t)(L > 0 ? L : 1) * OQ_D);
         oq_unpack_stream(cache + stream_ids[s] * stream_stride, L, kb, vb, kaxis_token,
                          groups_cap, kd, vd);
+        oq_attention(q + (int64_t)s * G * OQ_D, G, OQ_D, kd, vd, L, scale,
+                     out + (int64_t)s * G * OQ_D, lse + (int64_t)s * G);
+        free(kd);
+        free(vd);
+    }
+    return used;
+}
+
+/*
+ * One decode step of one layer from the oracle's own paged pool: for each
+ * listed (request, KV head), unpack its INT2 and INT4 tokens, then fp64
+ * attention of its G query rows. Returns the thread count used.
+ *   tables: int32 [n_req][max_pages]; req/head/n2/n4: per stream
+ *   q: fp16 [n_streams][G][128]; out: [n_streams][G][128]; lse: [n_streams][G]
+ */
+int oq_decode_paged(const uint8_t *pool, int n_streams, const int64_t *req, const int64_t *head,
+                    const int64_t *n2, const int64_t *n4, const int32_t *tables, int64_t max_pages,
+                    int32_t int2_pages, int hkv, const uint16_t *q, int G, double scale,
+                    double *out, double *lse, int nthreads)
+{
+    int used = 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+    {
+#pragma omp single
+        used = omp_get_num_threads();
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int s = 0; s < n_streams; ++s) {
+        int64_t L = n2[s] + n4[s];
+        float *kd = (float *)malloc(sizeof(float) * (size_t)(L > 0 ? L : 1) * OQ_D);
+        float *vd = (float *)malloc(sizeof(float) * (size_t)(L > 0 ? L : 1) * OQ_D);
+        oq_unpack_paged(pool, n2[s], n4[s], tables + req[s] * max_pages, int2_pages, hkv,
+                        (int)head[s], kd, vd);
         oq_attention(q + (int64_t)s * G * OQ_D, G, OQ_D, kd, vd, L, scale,
                      out + (int64_t)s * G * OQ_D, lse + (int64_t)s * G);
         free(kd);
