@@ -62,6 +62,16 @@ WORKLOADS = {
                                        desc="Qwen2.5-7B shape, batch 32, context 8192..8223, seeded "
                                             "9 x K8V4 + 19 x K4V2 (3.96 bits)"),
 }
+# Paged INT2/INT4 pool (TriAxialKV-style): every layer is a pool of 16-token pages; half of
+# each request's prompt tokens, in seeded 32-token runs, are INT2 (keys per-channel, values
+# per-token), the rest and every decoded token INT4 per-token; tables in seeded page order.
+PAGED_WORKLOADS = {
+    "paged-b16-l32768-int2int4": dict(layers=36, hq=32, hkv=8, batch=16, prefill=32767, cycle=32,
+                                      outliers=(4, 10.0),
+                                      desc="36 layers, 32/8 heads, batch 16, context 32768..32799 in a paged pool: "
+                                           "16384 INT2 tokens (seeded 32-token runs) + INT4 rest, 3.0 bits"),
+}
+WORKLOADS.update({k: dict(v, paged=True) for k, v in PAGED_WORKLOADS.items()})
 DEFAULT_WORKLOAD = "llama31-8b-b64-kivi8-trace"
 
 
@@ -150,6 +160,116 @@ class Workload:
         return total
 
 
+class PagedWorkload:
+    """A prefilled paged pool on the GPU plus the inputs of every decode step (same interface as
+    Workload). The prompt's INT2 runs go first in each request's page table, as the pool's page
+    tables require; decoded tokens are INT4."""
+
+    PAGE = 16
+
+    def __init__(self, name, seed=0, device="cuda", num_splits=0):
+        import torch
+
+        import layer_wise_mixed_amd as kvq
+
+        self.name, self.seed, self.kvq = name, seed, kvq
+        w = self.w = WORKLOADS[name]
+        self.L, self.B, self.Hq, self.Hkv = w["layers"], w["batch"], w["hq"], w["hkv"]
+        self.P, self.C = w["prefill"], w["cycle"]
+        self.outliers = w["outliers"]
+        self.scale = 1.0 / math.sqrt(128.0)
+        runs = self.P // 32
+        self.n2 = 32 * (runs // 2)  # INT2 tokens per request: half of the prompt's 32-token runs
+        n4_cap = self.P - self.n2 + self.C
+        pairs_per_req = self.n2 // 32
+        quads_per_req = -(-n4_cap // self.PAGE)
+        self.int2_pages = 2 * pairs_per_req * self.B
+        self.int4_pages = quads_per_req * self.B
+        self.max_pages = 2 * pairs_per_req + quads_per_req
+        shape = kvq.make_shape(self.Hq, self.Hkv, self.B, page_tokens=self.PAGE, int2_pages=self.int2_pages,
+                               int4_pages=self.int4_pages)
+        self.plan = kvq.plan_layers(shape, [(2, 2, 0, 1)] * self.L)
+        self.cache = torch.empty(self.plan.total_bytes, dtype=torch.uint8, device=device)
+        # seeded physical page order, one table per request (shared by all layers)
+        pairs = syn.seeded_permutation(seed, syn.T_PAGE, self.int2_pages // 2)
+        quads = syn.seeded_permutation(seed, syn.T_PAGE, self.int4_pages, salt=1)
+        table = []
+        for r in range(self.B):
+            row = [x for p in pairs[r * pairs_per_req:(r + 1) * pairs_per_req] for x in (2 * p, 2 * p + 1)]
+            row += [self.int2_pages + q for q in quads[r * quads_per_req:(r + 1) * quads_per_req]]
+            table.append(row)
+        self.table = torch.tensor(table, dtype=torch.int32, device=device)
+        self.num_splits = num_splits
+        zero = torch.zeros(self.B, dtype=torch.int32, device=device)
+        add2 = torch.full((self.B,), self.n2, dtype=torch.int32, device=device)
+        orders = [torch.tensor(self._prompt_order(r), dtype=torch.int64, device=device) for r in range(self.B)]
+        for l in range(self.L):  # prefill one request at a time: INT2 runs first, then the rest
+            for r in range(self.B):
+                order = orders[r]
+                k = self.keys(l, [r], 0, self.P, device).index_select(2, order)
+                v = syn.values_fp16(seed, l, [r], range(self.Hkv), 0, self.P, device=device).index_select(2, order)
+                pages = kvq.make_pages(self.table[r], self.max_pages, zero[r:], zero[r:], add2[r:])
+                kvq.quantize_append(self.plan, l, self.cache, k, v, None, pages)
+                del k, v
+        torch.cuda.synchronize()
+        self.k_dec, self.v_dec, self.q = [], [], []
+        for l in range(self.L):
+            k = self.keys(l, range(self.B), self.P, self.C, device)
+            v = syn.values_fp16(seed, l, range(self.B), range(self.Hkv), self.P, self.C, device=device)
+            self.k_dec.append(k.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
+            self.v_dec.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
+            qq = syn.queries_steps_fp16(seed, l, self.B, self.Hq, 0, self.C, device=device)
+            self.q.append(qq.permute(2, 0, 1, 3).contiguous())
+        self.n2_dev = torch.full((self.B,), self.n2, dtype=torch.int32, device=device)
+        self.n4_base = torch.full((self.B,), self.P - self.n2, dtype=torch.int32, device=device)
+        self.n4_before = self.n4_base.clone()
+        self.n4_after = self.n4_base + 1
+        self.pages_append = kvq.make_pages(self.table, self.max_pages, self.n2_dev, self.n4_before)
+        self.pages_decode = kvq.make_pages(self.table, self.max_pages, self.n2_dev, self.n4_after)
+        self.max_len = self.P + self.C
+        self.splits = num_splits or kvq.num_splits(self.plan, 0, self.B, self.max_len)
+        ws = kvq.workspace_bytes(self.plan, self.B, self.max_len, self.splits)
+        self.ws = torch.empty(ws // 4 + 1, dtype=torch.float32, device=device)
+        self.out = torch.empty(self.B, self.Hq, 128, dtype=torch.float16, device=device)
+        self.cfg = [(2, 2)] * self.L
+        torch.cuda.synchronize()
+
+    def _prompt_order(self, r):
+        """Token indices of request r's prompt in append order: its INT2 runs (seeded choice of
+        half of the 32-token runs, in arrival order), then every other token in arrival order."""
+        runs = self.P // 32
+        chosen = set(syn.seeded_choice(self.seed, syn.T_TAG, runs, self.n2 // 32, salt=r))
+        first = [t for j in sorted(chosen) for t in range(32 * j, 32 * j + 32)]
+        rest = [t for t in range(self.P) if t // 32 not in chosen or t >= 32 * runs]
+        return first + rest
+
+    def keys(self, layer, requests, t0, n, device):
+        cnt, fac = self.outliers
+        return syn.keys_fp16(self.seed, layer, requests, range(self.Hkv), t0, n, outlier_count=cnt,
+                             outlier_factor=fac, num_kv_heads=self.Hkv, device=device)
+
+    def reset(self):
+        self.n4_before.copy_(self.n4_base)
+        self.n4_after.copy_(self.n4_base)
+        self.n4_after.add_(1)
+
+    def step(self, i):
+        kvq = self.kvq
+        for l in range(self.L):
+            kvq.quantize_append(self.plan, l, self.cache, self.k_dec[l][i], self.v_dec[l][i], None, self.pages_append)
+            kvq.decode_attention(self.plan, l, self.cache, self.q[l][i], None, self.max_len, self.scale, self.out,
+                                 None, self.ws, self.splits, pages=self.pages_decode)
+        self.n4_before.add_(1)
+        self.n4_after.add_(1)
+
+    def split_bytes(self, i):
+        """Algorithmic bytes the split passes of step i read: INT2 group records (codes + meta),
+        INT4 tokens (codes + meta, 192 B per token and KV head), and q."""
+        n4 = self.P - self.n2 + i + 1
+        per_layer = self.B * self.Hkv * ((self.n2 // 32) * 4096 + n4 * 192) + self.B * self.Hq * 256
+        return per_layer * self.L
+
+
 def _source_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "layer_wise_mixed_amd", "csrc"))):
@@ -175,12 +295,58 @@ def _traffic(workload, achieved_bytes_per_launch):
 
 
 # -------------------------------------------------------------- CPU baseline
+def cpu_baseline_paged(wl, max_seconds=20.0):
+    """The oracle on a sample of the last decode step of a paged workload: it packs a sample of
+    (request, KV head) streams of layer 0 into its own pool through the same page tables, then
+    times unpack + dequantize + fp64 attention."""
+    import numpy as np
+
+    import oracle
+
+    n4 = wl.P - wl.n2 + wl.C  # INT4 tokens at the last step of the cycle
+    G = wl.Hq // wl.Hkv
+    layer = 0
+    n_streams = min(wl.B * wl.Hkv, 16)
+    pool = np.zeros(oracle.paged_pool_bytes(wl.Hkv, wl.int2_pages, wl.int4_pages), np.uint8)
+    tables = wl.table.cpu().numpy()
+    cnt, fac = wl.outliers
+    req, head, qs = [], [], np.zeros((n_streams, G, 128), np.float16)
+    for s in range(n_streams):
+        r, h = divmod(s, wl.Hkv)
+        order = wl._prompt_order(r) + list(range(wl.P, wl.P + wl.C))
+        k = syn.keys_fp16(wl.seed, layer, [r], [h], 0, wl.P + wl.C, outlier_count=cnt, outlier_factor=fac,
+                          num_kv_heads=wl.Hkv)[0, 0].numpy()[order]
+        v = syn.values_fp16(wl.seed, layer, [r], [h], 0, wl.P + wl.C)[0, 0].numpy()[order]
+        oracle.pack_paged(pool, k, v, wl.n2, tables[r], wl.int2_pages, wl.Hkv, h)
+        req.append(r)
+        head.append(h)
+        qs[s] = syn.queries_fp16(wl.seed, layer, wl.C - 1, r + 1, wl.Hq)[r, h * G:(h + 1) * G].numpy()
+    threads = min(os.cpu_count() or 1, 16)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        _, _, used = oracle.decode_paged(pool, req, head, [wl.n2] * n_streams, [n4] * n_streams, tables,
+                                         wl.int2_pages, wl.Hkv, qs, G, wl.scale, threads)
+        reps += 1
+        if time.perf_counter() - t0 > max_seconds or reps >= 1000:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    t_step = dt / n_streams * wl.B * wl.Hkv * wl.L
+    return {"value": wl.B / t_step, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{n_streams} (request, KV head) streams of layer 0 at {wl.n2} INT2 + {n4} INT4 tokens, "
+                      f"repeated {reps}x ({dt * 1e3:.1f} ms each); step time scaled to {wl.B * wl.Hkv} streams x "
+                      f"{wl.L} layers"}
+
+
 def cpu_baseline(wl, max_seconds=20.0):
     """The oracle, timed on host cores on a sample of the last decode step of the cycle:
     unpack + dequantize its own packed streams, then fp64 attention."""
     import numpy as np
 
     import oracle
+
+    if isinstance(wl, PagedWorkload):
+        return cpu_baseline_paged(wl, max_seconds)
 
     L = wl.P + wl.C  # the last step of the cycle
     G = wl.Hq // wl.Hkv
@@ -263,7 +429,8 @@ def main():
         return
     kvq.load()
     t_setup = time.perf_counter()
-    wl = Workload(args.workload, seed=args.seed, num_splits=args.splits)
+    cls = PagedWorkload if WORKLOADS[args.workload].get("paged") else Workload
+    wl = cls(args.workload, seed=args.seed, num_splits=args.splits)
     K = args.steps if args.steps is not None else wl.C
     W = args.warmup if args.warmup is not None else min(wl.C, 16)
     print(f"# setup {time.perf_counter() - t_setup:.1f}s: {wl.w['desc']}, splits={wl.splits}", file=sys.stderr,

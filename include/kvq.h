@@ -109,10 +109,18 @@ typedef struct kvq_plan {
 } kvq_plan;
 
 /* Paged-pool bookkeeping (device arrays, caller-owned). One page table per
- * request, shared by all layers; its first int2_len/16 entries are INT2
- * pages (aligned pairs 2k, 2k+1), the next ceil(int4_len/16) are INT4
- * pages. Page ids below shape.int2_pages index the INT2 region, the others
- * the INT4 region. */
+ * request, shared by all layers (TriAxialKV page, "Facts": each request's
+ * page table lists its INT2 pages before its INT4 pages). A page holds 16
+ * tokens of every KV head. Page ids below shape.int2_pages are INT2 pages
+ * (region at byte 0 of the layer, int2_page_bytes each); the others are INT4
+ * pages (region at int4_offset, the pool split, int4_page_bytes each).
+ * Entries 0 .. int2_len/16 - 1 hold the INT2 pages: a 32-token INT2 group
+ * (keys per-channel, values per-token, 2 bits) takes an aligned pair, entry
+ * 2i = its even id P and entry 2i+1 = P + 1. The next ceil(int4_len/16)
+ * entries hold the INT4 pages (keys and values per-token, 4 bits), entry
+ * int2_len/16 + t/16 holding INT4 token t. A request's tokens are its INT2
+ * tokens, then its INT4 tokens. Ids and lengths are trusted: the library
+ * does not check them on the device. */
 typedef struct kvq_pages {
     const int32_t *page_table; /* [batch][max_pages_per_req] */
     int32_t max_pages_per_req;
@@ -156,13 +164,19 @@ int kvq_plan_layers(const kvq_shape *shape, const kvq_layer_cfg *cfg, int32_t nu
  * per-token); the tokens past the last full group are kept in fp16 in the
  * stream's tail record. The call does not advance seq_lens: the caller
  * does. A stream whose length would pass max_tokens is left unchanged.
- * Paged mode (pages != NULL): the first int2_add[r] new tokens of request r
- * (a multiple of 32) are quantized into INT2 page pairs after int2_len[r];
- * the others, one token at a time, into INT4 pages after int4_len[r]
- * (TriAxialKV page, "Facts": leftover INT2 tokens go through the INT4
- * per-token path). The caller advances int2_len/int4_len.
- *   Errors: INVALID_ARG (null pointers, layer, batch, n_new out of range),
- *   CAPACITY (n_new > max_tokens), HIP.
+ * Paged mode (pages != NULL, required for a paged plan; seq_lens is then
+ * ignored): the first int2_add[r] new tokens of request r (a multiple of
+ * 32; int2_add NULL = 0) are quantized as INT2 groups into the page pairs
+ * that follow its int2_len[r] INT2 tokens; the others, each token on its
+ * own, into INT4 page slots after its int4_len[r] INT4 tokens (TriAxialKV
+ * page, "Facts": leftover INT2 tokens go through the INT4 per-token path).
+ * The page table must already hold its state after the call (the new INT2
+ * pairs at entries int2_len/16 .., the INT4 pages after all INT2 entries).
+ * A request whose int2_len or int2_add is not a multiple of 32 is left
+ * unchanged. The caller advances int2_len/int4_len.
+ *   Errors: INVALID_ARG (null pointers, layer, batch, n_new out of range,
+ *   pages given for a contiguous plan or missing for a paged one),
+ *   CAPACITY (n_new > max_tokens, or > 16 * max_pages_per_req), HIP.
  */
 int kvq_quantize_append(const kvq_plan *plan, int32_t layer, void *cache, const uint16_t *k_new,
                         const uint16_t *v_new, const int32_t *seq_lens, int32_t batch,
@@ -195,8 +209,14 @@ int32_t kvq_decode_num_splits(const kvq_plan *plan, int32_t layer, int32_t batch
  *   num_splits: 0 = automatic, else 1..1024.
  * A request with no tokens gets out = 0 and lse = -inf.
  * Paged mode (pages != NULL): lengths come from pages->int2_len/int4_len and
- * seq_lens is ignored; max_seq_len bounds int2_len + int4_len.
- *   Errors: INVALID_ARG, CAPACITY (max_seq_len > capacity), WORKSPACE, HIP.
+ * seq_lens is ignored; max_seq_len bounds int2_len + int4_len. Each split
+ * reads either INT2 groups or INT4 page pairs of one request, never both
+ * (TriAxialKV page, "Facts": INT2 pointers first give bitwidth-homogeneous
+ * splits), so a paged decode uses at least 2 splits and at most 256 groups
+ * of 32 tokens per split: num_splits >= 2 and
+ * (ceil(max_seq_len/32) + num_splits - 2) / (num_splits - 1) <= 256.
+ *   Errors: INVALID_ARG (including the split limits above), CAPACITY
+ *   (max_seq_len > max_tokens, or > 16 * max_pages_per_req), WORKSPACE, HIP.
  */
 int kvq_decode_attention(const kvq_plan *plan, int32_t layer, const void *cache,
                          const uint16_t *q, const int32_t *seq_lens, int32_t batch,
@@ -209,7 +229,8 @@ int kvq_decode_attention(const kvq_plan *plan, int32_t layer, const void *cache,
  * k_out, v_out: device fp32 [batch][Hkv][max_seq_len][128]; token j of
  * request r is fmaf(code, scale, zero) for quantized tokens and the stored
  * fp16 value for tail tokens; rows at or past the request's length are not
- * written. Paged mode lists INT2 tokens first, then INT4 tokens.
+ * written. Paged mode (pages != NULL; seq_lens ignored) lists each
+ * request's INT2 tokens first, then its INT4 tokens.
  *   Errors: INVALID_ARG, CAPACITY, HIP.
  */
 int kvq_dequantize(const kvq_plan *plan, int32_t layer, const void *cache,

@@ -103,10 +103,63 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+bool is_paged(const kvq_plan* plan) { return plan->shape.page_tokens != 0; }
+
+// Paged-pool view for the kernels; all zero in contiguous mode.
+kvq::PagedGeom paged_geom(const kvq_plan* plan, int32_t layer, const kvq_pages* pages) {
+  kvq::PagedGeom pg;
+  std::memset(&pg, 0, sizeof pg);
+  if (!pages) return pg;
+  const kvq_layer_plan& lp = plan->layers[layer];
+  pg.table = pages->page_table;
+  pg.int2_len = pages->int2_len;
+  pg.int4_len = pages->int4_len;
+  pg.int2_add = pages->int2_add;
+  pg.max_pages = pages->max_pages_per_req;
+  pg.int2_pages = plan->shape.int2_pages;
+  pg.int4_offset = lp.int4_offset;
+  pg.int2_page_bytes = lp.int2_page_bytes;
+  pg.int4_page_bytes = lp.int4_page_bytes;
+  return pg;
+}
+
+// pages must be given exactly for a paged plan, with its device arrays
+int check_pages(const kvq_plan* plan, const kvq_pages* pages) {
+  if (!is_paged(plan)) {
+    if (pages) return fail(KVQ_ERR_INVALID_ARG, "pages given for a contiguous plan");
+    return KVQ_OK;
+  }
+  if (!pages) return fail(KVQ_ERR_INVALID_ARG, "a paged plan needs pages");
+  if (!pages->page_table || !pages->int2_len || !pages->int4_len)
+    return fail(KVQ_ERR_INVALID_ARG, "pages: null page_table, int2_len or int4_len");
+  if (pages->max_pages_per_req <= 0)
+    return fail(KVQ_ERR_INVALID_ARG, "pages: max_pages_per_req %d", pages->max_pages_per_req);
+  return KVQ_OK;
+}
+
+// Token capacity of one request.
+int64_t capacity_tokens(const kvq_plan* plan, const kvq_pages* pages) {
+  return is_paged(plan) ? (int64_t)pages->max_pages_per_req * kvq::PAGE_TOKENS : plan->shape.max_tokens;
+}
+
+// A paged split walks at most 256 groups (64 per wave).
+constexpr int64_t kPagedMaxGroupsPerSplit = 256;
+
 int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
   const int64_t streams = (int64_t)batch * plan->shape.num_kv_heads;
   const int64_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
   if (nvg <= 0 || streams <= 0) return 1;
+  if (is_paged(plan)) {
+    // one kind per split: ceil(nvg / gps) + 1 splits cover a request's INT2
+    // groups and its INT4 page pairs together
+    int64_t s = (512 + streams - 1) / streams;
+    const int64_t s_min = (nvg + kPagedMaxGroupsPerSplit - 1) / kPagedMaxGroupsPerSplit;
+    if (s < s_min) s = s_min;
+    if (s > nvg) s = nvg;
+    const int64_t gps = (nvg + s - 1) / s;
+    const int64_t n = (nvg + gps - 1) / gps + 1;
+    return (int32_t)(n > 1024 ? 1024 : n);
+  }
   // 4-wave workgroups: aim for ~512 of them (2 per CU on 256 CUs), but keep
   // at least 8 groups (2 per wave) in each split
   int64_t s = (512 + streams - 1) / streams;
@@ -206,13 +259,14 @@ int kvq_quantize_append(const kvq_plan* plan, int32_t layer, void* cache, const 
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
   if (n_new < 0) return fail(KVQ_ERR_INVALID_ARG, "n_new %d < 0", n_new);
-  if (pages || plan->shape.page_tokens) return fail(KVQ_ERR_UNSUPPORTED, "paged append is not built yet");
-  if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
-  if (n_new > plan->shape.max_tokens)
-    return fail(KVQ_ERR_CAPACITY, "n_new %d > max_tokens %d", n_new, plan->shape.max_tokens);
+  if ((st = check_pages(plan, pages))) return st;
+  if (!pages && !seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (n_new > capacity_tokens(plan, pages))
+    return fail(KVQ_ERR_CAPACITY, "n_new %d > %lld tokens of capacity", n_new, (long long)capacity_tokens(plan, pages));
   if (batch == 0 || n_new == 0) return ok();
   kvq::AppendArgs a;
   a.geo = geom(plan, layer, cache);
+  a.pg = paged_geom(plan, layer, pages);
   a.k_new = k_new;
   a.v_new = v_new;
   a.seq_lens = seq_lens;
@@ -220,11 +274,14 @@ int kvq_quantize_append(const kvq_plan* plan, int32_t layer, void* cache, const 
   hipStream_t s = (hipStream_t)stream;
   kvq::EventPair ev;
   const bool timed = timer_slot(0, &ev);
-  return hip_status(kvq::launch_append(a, batch, s, timed ? &ev : nullptr), "append launch");
+  const hipError_t e = pages ? kvq::launch_append_paged(a, batch, s, timed ? &ev : nullptr)
+                             : kvq::launch_append(a, batch, s, timed ? &ev : nullptr);
+  return hip_status(e, "append launch");
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_plan* plan, int32_t batch, int32_t max_seq_len, int32_t num_splits) {
   if (!plan || batch < 0 || max_seq_len < 0 || num_splits < 0 || num_splits > 1024) return 0;
+  if (num_splits == 1 && is_paged(plan) && max_seq_len > 0) return 0;
   const int32_t s = num_splits ? num_splits : auto_splits(plan, batch, max_seq_len);
   return (size_t)batch * plan->shape.num_q_heads * s * (kvq::D + 1) * sizeof(float);
 }
@@ -249,22 +306,34 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   if (num_splits < 0 || num_splits > 1024) return fail(KVQ_ERR_INVALID_ARG, "num_splits %d", num_splits);
   if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
-  if (pages || plan->shape.page_tokens) return fail(KVQ_ERR_UNSUPPORTED, "paged decode is not built yet");
-  if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
-  if (max_seq_len > plan->shape.max_tokens)
-    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > max_tokens %d", max_seq_len, plan->shape.max_tokens);
+  if ((st = check_pages(plan, pages))) return st;
+  if (!pages && !seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (max_seq_len > capacity_tokens(plan, pages))
+    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > %lld tokens of capacity", max_seq_len,
+                (long long)capacity_tokens(plan, pages));
   if (batch == 0) return ok();
   const int32_t splits = num_splits ? num_splits : auto_splits(plan, batch, max_seq_len);
+  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
+  int32_t gps = nvg > 0 ? (nvg + splits - 1) / splits : 0;
+  if (pages && nvg == 0) gps = 1;  // no tokens anywhere; the kernels divide by gps
+  if (pages && nvg > 0) {
+    // a request's INT2 and INT4 parts start splits of their own: one split more
+    if (splits < 2) return fail(KVQ_ERR_INVALID_ARG, "a paged decode needs at least 2 splits");
+    gps = (nvg + splits - 2) / (splits - 1);
+    if (gps > kPagedMaxGroupsPerSplit)
+      return fail(KVQ_ERR_INVALID_ARG, "num_splits %d too small: a paged split walks at most %lld groups", splits,
+                  (long long)kPagedMaxGroupsPerSplit);
+  }
   const size_t need = (size_t)batch * plan->shape.num_q_heads * splits * (kvq::D + 1) * sizeof(float);
   if (!workspace || workspace_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
   kvq::DecodeArgs a;
   a.geo = geom(plan, layer, cache);
+  a.pg = paged_geom(plan, layer, pages);
   a.q = q;
   a.seq_lens = seq_lens;
   a.splits = splits;
-  a.groups_per_split = nvg > 0 ? (nvg + splits - 1) / splits : 0;
+  a.groups_per_split = gps;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.part_o = (float*)workspace;
   a.part_lse = a.part_o + (size_t)batch * plan->shape.num_q_heads * splits * kvq::D;
@@ -274,7 +343,8 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   hipStream_t s = (hipStream_t)stream;
   kvq::EventPair ev;
   bool timed = timer_slot(1, &ev);
-  hipError_t e = kvq::launch_decode_split_mfma(a, batch, s, timed ? &ev : nullptr);
+  hipError_t e = pages ? kvq::launch_decode_paged(a, batch, s, timed ? &ev : nullptr)
+                       : kvq::launch_decode_split_mfma(a, batch, s, timed ? &ev : nullptr);
   if (e != hipSuccess) return hip_status(e, "decode split launch");
   if (splits == 1) return ok();  // the split pass wrote the final output
   kvq::MergeArgs m;
@@ -298,18 +368,22 @@ int kvq_dequantize(const kvq_plan* plan, int32_t layer, const void* cache, const
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
   if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
-  if (pages || plan->shape.page_tokens) return fail(KVQ_ERR_UNSUPPORTED, "paged dequantize is not built yet");
-  if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
-  if (max_seq_len > plan->shape.max_tokens)
-    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > max_tokens %d", max_seq_len, plan->shape.max_tokens);
+  if ((st = check_pages(plan, pages))) return st;
+  if (!pages && !seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (max_seq_len > capacity_tokens(plan, pages))
+    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > %lld tokens of capacity", max_seq_len,
+                (long long)capacity_tokens(plan, pages));
   if (batch == 0 || max_seq_len == 0) return ok();
   kvq::DequantArgs a;
   a.geo = geom(plan, layer, cache);
+  a.pg = paged_geom(plan, layer, pages);
   a.seq_lens = seq_lens;
   a.max_seq_len = max_seq_len;
   a.k_out = k_out;
   a.v_out = v_out;
-  return hip_status(kvq::launch_dequant(a, batch, (hipStream_t)stream), "dequantize launch");
+  const hipError_t e = pages ? kvq::launch_dequant_paged(a, batch, (hipStream_t)stream)
+                             : kvq::launch_dequant(a, batch, (hipStream_t)stream);
+  return hip_status(e, "dequantize launch");
 }
 
 int kvq_timer_start(int32_t capacity) {

@@ -77,6 +77,46 @@ __device__ inline void pack_block(uint8_t* blk, const uint16_t (*codes)[D], int 
   }
 }
 
+// Quantize one full 32-token group (xs: fp16 K and V [32][128], in LDS) and
+// write its record; cs is LDS scratch for the codes. 256 threads.
+__device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][D], uint8_t* rec, int kb,
+                                       int vb, int k_token, int tid) {
+  const RecordParts parts = record_parts(kb, vb);
+  float* kmeta = (float*)(rec + parts.kmeta);
+  float* vmeta = (float*)(rec + parts.vmeta);
+  if (tid < 128) {
+    if (kb == 16) {
+      for (int i = 0; i < GS; ++i) cs[0][i][tid] = xs[0][i][tid];
+    } else if (!k_token) {
+      const int c = tid;
+      float s, z;
+      quantize32(&xs[0][0][c], D, kb, &cs[0][0][c], D, &s, &z);
+      kmeta[meta_channel(c)] = s;
+      kmeta[128 + meta_channel(c)] = z;
+    } else {
+      const int j = tid >> 2, n = tid & 3;
+      float s, z;
+      quantize32(&xs[0][j][32 * n], 1, kb, &cs[0][j][32 * n], 1, &s, &z);
+      kmeta[meta_token(j, n)] = s;
+      kmeta[128 + meta_token(j, n)] = z;
+    }
+  } else {
+    const int t2 = tid - 128;
+    if (vb == 16) {
+      for (int i = 0; i < GS; ++i) cs[1][i][t2] = xs[1][i][t2];
+    } else {
+      const int j = t2 >> 2, n = t2 & 3;
+      float s, z;
+      quantize32(&xs[1][j][32 * n], 1, vb, &cs[1][j][32 * n], 1, &s, &z);
+      vmeta[meta_token(j, n)] = s;
+      vmeta[128 + meta_token(j, n)] = z;
+    }
+  }
+  __syncthreads();
+  pack_block(rec, cs[0], kb, false, tid, blockDim.x);
+  pack_block(rec + parts.vcode, cs[1], vb, true, tid, blockDim.x);
+}
+
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ uint16_t xs[2][GS][D];
   __shared__ uint16_t cs[2][GS][D];
@@ -112,41 +152,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       xs[1][i][c] = vv;
     }
     __syncthreads();
-    uint8_t* rec = stream + (size_t)m * g.record_bytes;
-    const RecordParts parts = record_parts(g.kb, g.vb);
-    float* kmeta = (float*)(rec + parts.kmeta);
-    float* vmeta = (float*)(rec + parts.vmeta);
-    if (tid < 128) {
-      if (g.kb == 16) {
-        for (int i = 0; i < GS; ++i) cs[0][i][tid] = xs[0][i][tid];
-      } else if (!g.k_token) {
-        const int c = tid;
-        float s, z;
-        quantize32(&xs[0][0][c], D, g.kb, &cs[0][0][c], D, &s, &z);
-        kmeta[meta_channel(c)] = s;
-        kmeta[128 + meta_channel(c)] = z;
-      } else {
-        const int j = tid >> 2, n = tid & 3;
-        float s, z;
-        quantize32(&xs[0][j][32 * n], 1, g.kb, &cs[0][j][32 * n], 1, &s, &z);
-        kmeta[meta_token(j, n)] = s;
-        kmeta[128 + meta_token(j, n)] = z;
-      }
-    } else {
-      const int t2 = tid - 128;
-      if (g.vb == 16) {
-        for (int i = 0; i < GS; ++i) cs[1][i][t2] = xs[1][i][t2];
-      } else {
-        const int j = t2 >> 2, n = t2 & 3;
-        float s, z;
-        quantize32(&xs[1][j][32 * n], 1, g.vb, &cs[1][j][32 * n], 1, &s, &z);
-        vmeta[meta_token(j, n)] = s;
-        vmeta[128 + meta_token(j, n)] = z;
-      }
-    }
-    __syncthreads();
-    pack_block(rec, cs[0], g.kb, false, tid, blockDim.x);
-    pack_block(rec + parts.vcode, cs[1], g.vb, true, tid, blockDim.x);
+    quantize_record(xs, cs, stream + (size_t)m * g.record_bytes, g.kb, g.vb, g.k_token, tid);
   }
   if (y == 0) {
     __syncthreads();  // the flush above has read the old tail slots
@@ -203,7 +209,155 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   }
 }
 
+// Paged append, one workgroup per (block x, request, KV head). Blocks
+// x < n_new / 32 quantize INT2 group x (new tokens 32x .. 32x+31, when they
+// are among the request's first int2_add[r] new tokens) into its page pair;
+// the others write INT4 page int4_len[r] / 16 + (x - n_new / 32) with the new
+// INT4 tokens that fall in it (TriAxialKV page, "Facts": leftover INT2
+// tokens take the INT4 per-token path).
+__global__ __launch_bounds__(256) void paged_append_kernel(AppendArgs a) {
+  __shared__ uint16_t xs[2][GS][D];
+  __shared__ uint16_t cs[2][GS][D];
+  const LayerGeom& g = a.geo;
+  const PagedGeom& pg = a.pg;
+  const int tid = threadIdx.x;
+  const int x = blockIdx.x;
+  const int sigma = blockIdx.y;
+  const int r = sigma / g.hkv, h = sigma % g.hkv;
+  const int n2_old = pg.int2_len[r], n4_old = pg.int4_len[r];
+  const int add2 = pg.int2_add ? pg.int2_add[r] : 0;
+  if (n2_old < 0 || n4_old < 0 || add2 < 0 || add2 > a.n_new || (add2 % GS) != 0 || (n2_old % GS) != 0) return;
+  const int32_t* table = pg.table + (size_t)r * pg.max_pages;
+  const uint16_t* kn = a.k_new + (size_t)sigma * a.n_new * D;
+  const uint16_t* vn = a.v_new + (size_t)sigma * a.n_new * D;
+  const int x2 = a.n_new / GS;
+
+  if (x < x2) {  // ------------------------------------------- INT2 group
+    if (GS * (x + 1) > add2) return;
+    for (int idx = tid; idx < GS * D; idx += blockDim.x) {
+      const int i = idx >> 7, c = idx & 127;
+      xs[0][i][c] = kn[(size_t)(GS * x + i) * D + c];
+      xs[1][i][c] = vn[(size_t)(GS * x + i) * D + c];
+    }
+    __syncthreads();
+    const int pair = table[(n2_old + GS * x) / PAGE_TOKENS];
+    uint8_t* rec = g.base + (size_t)pair * pg.int2_page_bytes + (size_t)h * INT2_RECORD;
+    quantize_record(xs, cs, rec, 2, 2, 0, tid);
+    return;
+  }
+
+  // ------------------------------------------------------ one INT4 page
+  const int n4_add = a.n_new - add2;
+  const int P = n4_old / PAGE_TOKENS + (x - x2);
+  const int t_lo = max(n4_old, PAGE_TOKENS * P), t_hi = min(n4_old + n4_add, PAGE_TOKENS * (P + 1));
+  if (t_lo >= t_hi) return;
+  const int p_lo = t_lo - PAGE_TOKENS * P, p_hi = t_hi - PAGE_TOKENS * P;  // slots written
+  const int id = table[(n2_old + add2) / PAGE_TOKENS + P];
+  uint8_t* page = g.base + pg.int4_offset + (size_t)(id - pg.int2_pages) * pg.int4_page_bytes + (size_t)h * INT4_HEAD;
+  for (int idx = tid; idx < PAGE_TOKENS * D; idx += blockDim.x) {
+    const int p = idx >> 7, c = idx & 127;
+    if (p < p_lo || p >= p_hi) continue;
+    const size_t i = (size_t)(add2 + PAGE_TOKENS * P + p - n4_old);  // index among the new tokens
+    xs[0][p][c] = kn[i * D + c];
+    xs[1][p][c] = vn[i * D + c];
+  }
+  __syncthreads();
+  if (tid < 128) {  // per-token quantization: (tensor, slot, channel group)
+    const int tensor = tid >> 6, p = (tid >> 2) & 15, n = tid & 3;
+    if (p >= p_lo && p < p_hi) {
+      float s, z;
+      quantize32(&xs[tensor][p][32 * n], 1, 4, &cs[tensor][p][32 * n], 1, &s, &z);
+      float* meta = (float*)(page + (tensor ? INT4_VMETA : INT4_KMETA));
+      meta[16 * n + p] = s;
+      meta[64 + 16 * n + p] = z;
+    }
+  }
+  __syncthreads();
+  {  // key words: the 8 codes of a word belong to one slot
+    const int p = tid >> 4, a4 = (tid >> 2) & 3, w = tid & 3;
+    if (p >= p_lo && p < p_hi) {
+      uint32_t word = 0;
+      for (int pos = 0; pos < 8; ++pos) {
+        int sh;
+        const int c = 32 * w + 8 * a4 + pos;
+        (void)page_k_offset(p, c, &sh);
+        word |= (uint32_t)cs[0][p][c] << sh;
+      }
+      int sh0;
+      *(uint32_t*)(page + page_k_offset(p, 32 * w + 8 * a4, &sh0)) = word;
+    }
+  }
+  {  // value words: four slots share a word; keep the slots not written now
+    const int quad = tid >> 6, c16 = (tid >> 2) & 15, wv = tid & 3;
+    if (4 * quad + 3 >= p_lo && 4 * quad < p_hi) {
+      int sh;
+      const uint32_t off = page_v_offset(4 * quad, 32 * wv + c16, &sh);
+      uint32_t word = (4 * quad < p_lo || 4 * quad + 3 >= p_hi) ? *(const uint32_t*)(page + off) : 0u;
+      for (int i = 0; i < 4; ++i) {
+        const int p = 4 * quad + i;
+        if (p < p_lo || p >= p_hi) continue;
+        for (int hh = 0; hh < 2; ++hh) {
+          const int c = 16 * (2 * wv + hh) + c16;
+          (void)page_v_offset(p, c, &sh);
+          word = (word & ~(0xFu << sh)) | ((uint32_t)cs[1][p][c] << sh);
+        }
+      }
+      *(uint32_t*)(page + off) = word;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void paged_dequant_kernel(DequantArgs a) {
+  const LayerGeom& g = a.geo;
+  const PagedGeom& pg = a.pg;
+  const int m = blockIdx.x;
+  const int sigma = blockIdx.y;
+  const int r = sigma / g.hkv, h = sigma % g.hkv;
+  const int n2 = pg.int2_len[r], n4 = pg.int4_len[r];
+  if (n2 < 0 || n4 < 0 || (n2 % GS) != 0) return;
+  const int lw = min(n2 + n4, a.max_seq_len);
+  const int32_t* table = pg.table + (size_t)r * pg.max_pages;
+  const RecordParts parts = record_parts(2, 2);
+  for (int idx = threadIdx.x; idx < GS * D; idx += blockDim.x) {
+    const int t = m * GS + (idx >> 7), c = idx & 127;
+    if (t >= lw) continue;
+    const size_t o = ((size_t)sigma * a.max_seq_len + t) * D + c;
+    if (t < n2) {
+      const uint8_t* rec =
+          g.base + (size_t)table[t / PAGE_TOKENS & ~1] * pg.int2_page_bytes + (size_t)h * INT2_RECORD;
+      a.k_out[o] = read_elem(rec, parts, 2, 2, 0, false, t % GS, c);
+      a.v_out[o] = read_elem(rec, parts, 2, 2, 0, true, t % GS, c);
+    } else {
+      const int u = t - n2, p = u % PAGE_TOKENS;
+      const uint8_t* page = g.base + pg.int4_offset +
+                            (size_t)(table[n2 / PAGE_TOKENS + u / PAGE_TOKENS] - pg.int2_pages) * pg.int4_page_bytes +
+                            (size_t)h * INT4_HEAD;
+      const float* km = (const float*)(page + INT4_KMETA);
+      const float* vm = (const float*)(page + INT4_VMETA);
+      const int mi = 16 * (c >> 5) + p;
+      int sh;
+      uint32_t off = page_k_offset(p, c, &sh);
+      a.k_out[o] = fmaf((float)((*(const uint32_t*)(page + off) >> sh) & 15u), km[mi], km[64 + mi]);
+      off = page_v_offset(p, c, &sh);
+      a.v_out[o] = fmaf((float)((*(const uint32_t*)(page + off) >> sh) & 15u), vm[mi], vm[64 + mi]);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_paged(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev) {
+  if (a.n_new == 0 || batch == 0) return hipSuccess;
+  const int x = a.n_new / GS + (a.n_new + PAGE_TOKENS - 1) / PAGE_TOKENS + 1;
+  return launch_timed(paged_append_kernel, dim3(x, batch * a.geo.hkv), dim3(256), s, ev, a);
+}
+
+hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s) {
+  const int y = (a.max_seq_len + GS - 1) / GS;
+  if (y == 0 || batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(paged_dequant_kernel, dim3(y, batch * a.geo.hkv), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev) {
   const int y = a.n_new > 0 ? (a.n_new + GS - 1) / GS : 0;

@@ -18,6 +18,23 @@
 // 32*((c/8)%4) + 8*(c/32) + c%8, per-token index 32*n + kappa(j),
 // kappa(j) = 8*((j%16)/4) + 4*(j/16) + j%4.
 // A stream is groups_cap records then one tail record in the K16V16 format.
+//
+// Paged pool (TriAxialKV page, "Facts": INT2 and INT4 page pools in one
+// address space split at an offset; INT4 keys and values per-token). Pages
+// hold 16 tokens of every KV head; ids below int2_pages are INT2 pages.
+//   INT2: an aligned page pair (P even, P + 1) holds one K2V2 record (keys
+//         per-channel) per KV head, head h at P * int2_page_bytes + h * 4096.
+//   INT4: page P, head h at int4_offset + (P - int2_pages) * int4_page_bytes
+//         + h * 3072: [K codes 1 KiB][V codes 1 KiB][K meta 512][V meta 512]
+//         for slots p = 0..15, 4-bit codes, lane word w at lane * 16 + w * 4.
+//         K (p, c): lane 16*((c/8)%4) + p, word c/32, position c%8 (the
+//         token half of a K4V4 record's key block); V (p, c): lane
+//         16*(p/4) + c%16, word (c/16)/2, bit 8*((c/16)%2) + 4*((p%4)/2) +
+//         16*(p%2), so that two pages' words interleave bytewise into the V
+//         words of a 32-token record. Meta: 64 scales then 64 zeros, index
+//         16*(c/32) + p.
+// A request's page table lists its INT2 pairs (entry 2i = even id of group i)
+// and then its INT4 pages (entry int2_len/16 + t/16 holds INT4 token t).
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -93,7 +110,37 @@ __host__ __device__ inline RecordParts record_parts(int kb, int vb) {
   return p;
 }
 
+constexpr int PAGE_TOKENS = 16;
+constexpr int INT2_RECORD = 4096;  // K2V2 record of one KV head in a page pair
+constexpr int INT4_HEAD = 3072;    // one KV head's share of an INT4 page
+constexpr int INT4_VCODE = 1024, INT4_KMETA = 2048, INT4_VMETA = 2560;
+
+__host__ __device__ inline uint32_t page_k_offset(int p, int c, int* shift) {
+  const int pos = c & 7;
+  *shift = 16 * (pos & 1) + 4 * (pos >> 1);
+  return (uint32_t)(16 * ((c >> 3) & 3) + p) * 16u + (uint32_t)(c >> 5) * 4u;
+}
+
+__host__ __device__ inline uint32_t page_v_offset(int p, int c, int* shift) {
+  const int u = c >> 4;
+  *shift = 8 * (u & 1) + 4 * ((p & 3) >> 1) + 16 * (p & 1);
+  return INT4_VCODE + (uint32_t)(16 * (p >> 2) + (c & 15)) * 16u + (uint32_t)(u >> 1) * 4u;
+}
+
 // ------------------------------------------------------------ launch args
+
+// Paged-pool view of one layer (all pointers device, caller-owned).
+struct PagedGeom {
+  const int32_t* table;     // [batch][max_pages]; null = contiguous mode
+  const int32_t* int2_len;  // [batch]
+  const int32_t* int4_len;  // [batch]
+  const int32_t* int2_add;  // append: [batch] or null (= 0)
+  int max_pages;
+  int int2_pages;
+  uint64_t int4_offset;
+  uint64_t int2_page_bytes;
+  uint64_t int4_page_bytes;
+};
 
 struct LayerGeom {
   uint8_t* base;          // layer region
@@ -108,6 +155,7 @@ struct LayerGeom {
 
 struct AppendArgs {
   LayerGeom geo;
+  PagedGeom pg;
   const uint16_t* k_new;
   const uint16_t* v_new;
   const int32_t* seq_lens;
@@ -116,6 +164,7 @@ struct AppendArgs {
 
 struct DequantArgs {
   LayerGeom geo;
+  PagedGeom pg;
   const int32_t* seq_lens;
   int max_seq_len;
   float* k_out;
@@ -124,6 +173,7 @@ struct DequantArgs {
 
 struct DecodeArgs {
   LayerGeom geo;
+  PagedGeom pg;
   const uint16_t* q;
   const int32_t* seq_lens;
   int splits;
@@ -155,6 +205,9 @@ struct EventPair {
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s);
 hipError_t launch_decode_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
+hipError_t launch_decode_paged(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
+hipError_t launch_append_paged(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev);
+hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, const EventPair* ev);
 
 // kernel launch with optional dispatch-bound events

@@ -145,7 +145,7 @@ __device__ inline float bpermute(int addr, float v) {
 }
 
 struct Lane {
-  int lane, la, gcol, slot;
+  int lane, la, gcol, slot, g;
   bool col_ok;
   const float* qv;  // LDS: q' of the lane's row at channels 32 s + 8 la + i is qv[32 s + i]
   float qn[4];      // per 32-channel group sums of q' (per-token keys)
@@ -256,9 +256,25 @@ __device__ __forceinline__ void raise_max(float bm, Acc& acc) {
   }
 }
 
+// The P.V operand of value tile u (channels 16u..16u+15). VPAGE: vw holds the
+// V words of two INT4 pages, [page a words 0..3][page b words 0..3]; the
+// record word u is bytes h, h+2 of page a's word u/2 interleaved with the same
+// bytes of page b's (h = u % 2).
+template <int VB, bool VPAGE>
+__device__ __forceinline__ h8_t value_operand(const uint32_t* vw, int u) {
+  if constexpr (VPAGE) {
+    const uint32_t x = vw[u >> 1], y = vw[4 + (u >> 1)];
+    const uint32_t w = (u & 1) ? (((x >> 8) & 0x00FF00FFu) | (y & 0xFF00FF00u))
+                               : ((x & 0x00FF00FFu) | ((y << 8) & 0xFF00FF00u));
+    return unpack8<4>(&w, 0);
+  } else {
+    return unpack8<VB>(vw, u);
+  }
+}
+
 // p = exp2(score - max) of one group, and its P.V products. VB: value code
 // width; vmeta: LDS copy of the group's value meta.
-template <int VB, int NS, bool TAIL>
+template <int VB, int NS, bool TAIL, bool VPAGE = false>
 __device__ __forceinline__ void group_pv(const uint32_t* vw, const float* vmeta, int ntok, const float* sc,
                                          const Lane& ln, Acc& acc) {
   float p[8];
@@ -296,7 +312,7 @@ __device__ __forceinline__ void group_pv(const uint32_t* vw, const float* vmeta,
     // the two 16-channel tiles of each of channel groups pass*NS .. pass*NS + NS - 1
 #pragma unroll
     for (int u = 2 * pass * NS; u < 2 * (pass + 1) * NS; ++u) {
-      h8_t A = unpack8<VB>(vw, u);
+      h8_t A = value_operand<VB, VPAGE>(vw, u);
       if constexpr (TAIL) {
         u4_t x = __builtin_bit_cast(u4_t, A);
         x &= vmask;
@@ -308,7 +324,7 @@ __device__ __forceinline__ void group_pv(const uint32_t* vw, const float* vmeta,
   }
 }
 
-template <int KB, int VB, bool KTOK, int NS, bool TAIL>
+template <int KB, int VB, bool KTOK, int NS, bool TAIL, bool VPAGE = false>
 __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t* vw, const float* kmeta,
                                               const float* vmeta, int ntok, const h8_t* bh, const h8_t* bl,
                                               float beta, int src, const Lane& ln, Acc& acc) {
@@ -316,49 +332,39 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
   group_scores<KB, KTOK, TAIL>(kw, kmeta, ntok, bh, bl, beta, src, ln, sc);
   raise_max(fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))),
             acc);
-  group_pv<VB, NS, TAIL>(vw, vmeta, ntok, sc, ln, acc);
+  group_pv<VB, NS, TAIL, VPAGE>(vw, vmeta, ntok, sc, ln, acc);
 }
 
-template <int KB, int VB, bool KTOK, int NS>
-__global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
-  constexpr bool STACK = KB < 16 && !KTOK;  // per-channel keys: one B operand for NS groups
-  constexpr int R = STACK ? NS : 1;
-  constexpr int NKW = 2 * KB, NVW = 2 * VB;
-  constexpr int KM = R;  // key meta records staged per refresh
-  __shared__ float s_kmeta[kWaves][KM][256];
-  __shared__ float s_vmeta[kWaves][256];
-  __shared__ float s_o[kWaves][kMaxG][D];
-  __shared__ float s_ml[kWaves][2][kMaxG];
-  __shared__ float s_q[kMaxG][D];
-  const LayerGeom& g = a.geo;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-  const int G = g.g;
-  int L = a.seq_lens[r];
-  if (L < 0) L = 0;
-  if (L > g.max_tokens) L = g.max_tokens;
-  const int nq = L / GS;
-  const int T = L - nq * GS;
-  const int nvg = nq + (T > 0);
-  const int g0 = split * a.groups_per_split;
-  const int g1 = min(g0 + a.groups_per_split, nvg);
-  const int sigma = r * g.hkv + h;
-  const uint8_t* stream = g.base + (size_t)sigma * g.stream_bytes;
+// Every member is a multiple of 16 bytes long, so with the struct aligned
+// each member is too (LDS reads of q', meta and results stay 16 bytes wide).
+template <int R>
+struct alignas(16) SplitSmem {
+  float kmeta[kWaves][R][256];  // per wave: the key meta of up to R groups
+  float vmeta[kWaves][256];     // per wave: the value meta of the current group
+  float o[kWaves][kMaxG][D];    // per wave: its result, for the combine
+  float ml[kWaves][2][kMaxG];
+  float q[kMaxG][D];            // q' of the G query rows
+};
 
-  Lane ln;
+// The lane's roles, q' = q * softmax_scale * log2(e) of the G rows into LDS,
+// and (per-token keys) the sums of q' over each 32-channel group.
+template <int NS, bool QN>
+__device__ __forceinline__ void setup_lane(const DecodeArgs& a, int r, int h, float (*s_q)[D], Lane& ln, Acc& acc) {
+  const int tid = threadIdx.x;
+  const int G = a.geo.g;
   ln.lane = tid & 63;
   ln.la = ln.lane >> 4;
+  ln.g = G;
   const int c16 = ln.lane & 15;
   ln.gcol = c16 % G;
   ln.slot = c16 / G;
   ln.col_ok = ln.slot < NS;
   for (int idx = tid; idx < G * D; idx += blockDim.x)
-    s_q[idx >> 7][idx & 127] = (float)__builtin_bit_cast(_Float16, a.q[((size_t)r * g.hq + h * G) * D + idx]) *
+    s_q[idx >> 7][idx & 127] = (float)__builtin_bit_cast(_Float16, a.q[((size_t)r * a.geo.hq + h * G) * D + idx]) *
                                a.scale_log2;
   __syncthreads();
   ln.qv = &s_q[ln.gcol][8 * ln.la];
-  if constexpr (KTOK && KB < 16) {
+  if constexpr (QN) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       float part = 0.f;
@@ -367,7 +373,6 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
       ln.qn[s] = sum_lane_groups(part);
     }
   }
-  Acc acc;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     acc.o[u] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -377,12 +382,240 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   acc.lpart = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) acc.zpart[k] = 0.f;
-  float* kmeta = &s_kmeta[wave][0][0];
-  float* vmeta = s_vmeta[wave];
+}
 
-  // ------------------------------------ the tail group first, in true units
-  const bool has_tail = T > 0 && nq >= g0 && nq < g1;
-  if (has_tail && ((nq - g0) & (kWaves - 1)) == wave) {
+// Each wave's result into LDS, the four waves combined, and the split's
+// output written: the final output when it is the only split, else the
+// split's partial (o, lse) for the merge pass. VB: the value code width the
+// wave's accumulators are in.
+template <int VB, int NS, int R>
+__device__ __forceinline__ void finish(const DecodeArgs& a, int r, int h, int split, int wave, SplitSmem<R>& sm,
+                                       const Lane& ln, Acc& acc) {
+  const int tid = threadIdx.x;
+  const int G = a.geo.g;
+  const float l = sum_lane_groups(acc.lpart);
+  const float vmul = code_scale<VB>();
+#pragma unroll
+  for (int pass = 0; pass < 4 / NS; ++pass) {
+    const float z = sum_lane_groups(acc.zpart[pass]);
+    // the lane's column holds channel group n = pass * NS + slot: tiles 2n, 2n + 1
+    // (picked by selects: a runtime index would send the accumulators to scratch)
+    f4_t o[2], ol[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      o[t] = acc.o[2 * pass * NS + t];
+      ol[t] = acc.ol[2 * pass * NS + t];
+#pragma unroll
+      for (int q = 1; q < NS; ++q) {
+        const bool take = ln.slot == q;
+        o[t] = take ? acc.o[2 * (pass * NS + q) + t] : o[t];
+        ol[t] = take ? acc.ol[2 * (pass * NS + q) + t] : ol[t];
+      }
+    }
+    if (ln.col_ok) {
+      const int n = pass * NS + ln.slot;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sm.o[wave][ln.gcol][32 * n + 16 * t + 4 * ln.la + i] = fmaf(fmaf(ol[t][i], kLoDown, o[t][i]), vmul, z);
+    }
+  }
+  if (ln.lane < G) {
+    sm.ml[wave][0][ln.lane] = acc.m;
+    sm.ml[wave][1][ln.lane] = l;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+    const int gg = idx >> 7, c = idx & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.ml[w][0][gg]);
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.ml[w][0][gg];
+        if (mw == -INFINITY) continue;
+        const float e = __builtin_amdgcn_exp2f(mw - M);
+        num = fmaf(e, sm.o[w][gg][c], num);
+        den = fmaf(e, sm.ml[w][1][gg], den);
+      }
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    const float lse = den > 0.f ? (M + __log2f(den)) * 0.69314718055994531f : -INFINITY;
+    const size_t qrow = (size_t)r * a.geo.hq + h * G + gg;
+    if (a.splits == 1) {  // the only split: final output
+      if (a.out_f32)
+        ((float*)a.out)[qrow * D + c] = o;
+      else
+        ((_Float16*)a.out)[qrow * D + c] = (_Float16)o;
+      if (c == 0 && a.lse_out) a.lse_out[qrow] = lse;
+    } else {
+      const size_t row = qrow * a.splits + split;
+      a.part_o[row * D + c] = o;
+      if (c == 0) a.part_lse[row] = lse;
+    }
+  }
+}
+
+// ---------------------------------------------------------- group sources
+// Where the wave's k-th packed group lives. Each source loads a lane's code
+// words (and, for per-token values, its 16 bytes of value meta) and its 16
+// bytes of key meta, in the layout of a 32-token record.
+
+// Records first, first + 4, first + 8, ... of one contiguous stream.
+template <int KB, int VB>
+struct StreamSrc {
+  const uint8_t* first;  // the wave's first record
+  uint32_t stride;       // kWaves records
+  RecordParts parts;
+  static constexpr bool kVPage = false;
+  __device__ const uint8_t* rec(int k) const { return first + (size_t)k * stride; }
+  __device__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
+    const uint8_t* r = rec(k);
+    load_codes<KB>(r, lane, kw);
+    load_codes<VB>(r + parts.vcode, lane, vw);
+    if constexpr (VB < 16) vm = *(const u4_t*)(r + parts.vmeta + lane * 16);
+  }
+  __device__ u4_t kmeta(int k, int lane) const { return *(const u4_t*)(rec(k) + parts.kmeta + lane * 16); }
+};
+
+// INT2 groups of a paged request: the K2V2 record of one KV head in the page
+// pair of group first + 4 k. ids: lane i holds the even page id of the wave's
+// group i (i < 64).
+struct Int2Src {
+  const uint8_t* base;  // pool + h * 4096
+  uint64_t page_bytes;
+  int ids;
+  static constexpr bool kVPage = false;
+  __device__ const uint8_t* rec(int k) const {
+    return base + (size_t)__builtin_amdgcn_readlane(ids, k) * page_bytes;
+  }
+  __device__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
+    const uint8_t* r = rec(k);
+    load_codes<2>(r, lane, kw);
+    load_codes<2>(r + 1024, lane, vw);
+    vm = *(const u4_t*)(r + 3072 + lane * 16);
+  }
+  __device__ u4_t kmeta(int k, int lane) const { return *(const u4_t*)(rec(k) + 2048 + lane * 16); }
+};
+
+// INT4 page pairs of a paged request: group i is the pages of table entries
+// 2i, 2i + 1 of its INT4 part (tokens 32 i .. 32 i + 31). ida/idb: lane i
+// holds the two pages' region indices for the wave's group i (i < 64).
+struct Int4Src {
+  const uint8_t* base;  // INT4 region + h * 3072
+  uint64_t page_bytes;
+  int ida, idb;
+  static constexpr bool kVPage = true;
+  __device__ const uint8_t* page(int id) const { return base + (size_t)id * page_bytes; }
+  __device__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
+    const uint8_t* pa = page(__builtin_amdgcn_readlane(ida, k));
+    const uint8_t* pb = page(__builtin_amdgcn_readlane(idb, k));
+    load_codes<2>(pa, lane, kw);  // one 16-byte row per page: key words 0..3 and 4..7
+    load_codes<2>(pb, lane, kw + 4);
+    load_codes<2>(pa + INT4_VCODE, lane, vw);
+    load_codes<2>(pb + INT4_VCODE, lane, vw + 4);
+    vm = *(const u4_t*)(meta_site(pa, pb, lane) + INT4_VMETA);
+  }
+  // lane l's 16 bytes of a record's per-token meta (record floats 4l .. 4l+3)
+  // come from page l % 2: scales for l < 32, zeros after, channel group
+  // (l % 32) / 8, slots 4 ((l % 8) / 2) + 0..3
+  __device__ static const uint8_t* meta_site(const uint8_t* pa, const uint8_t* pb, int lane) {
+    return ((lane & 1) ? pb : pa) + (lane >> 5) * 256 + ((lane & 31) >> 1) * 16;
+  }
+  __device__ u4_t kmeta(int k, int lane) const {
+    const uint8_t* pa = page(__builtin_amdgcn_readlane(ida, k));
+    const uint8_t* pb = page(__builtin_amdgcn_readlane(idb, k));
+    return *(const u4_t*)(meta_site(pa, pb, lane) + INT4_KMETA);
+  }
+};
+
+// The wave's nk packed groups from `src`, one group loading ahead in a second
+// register buffer; the loop is unrolled by two so every buffer index is
+// static (no register copies).
+template <int KB, int VB, bool KTOK, int NS, int R, class Src>
+__device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta, float* vmeta, const Lane& ln,
+                                           Acc& acc) {
+  constexpr bool STACK = KB < 16 && !KTOK;  // per-channel keys: one B operand for R groups
+  constexpr int NKW = 2 * KB, NVW = 2 * VB;
+  constexpr bool VPAGE = Src::kVPage;
+  if (nk <= 0) return;
+  struct Buf {
+    uint32_t kw[NKW];
+    uint32_t vw[NVW];
+    u4_t vm;
+  };
+  Buf buf[2];
+  u4_t kmr[R];
+  h8_t bh[4], bl[4];
+  float beta = 0.f;
+  if constexpr (!STACK) q_operands(ln, bh, bl);
+  src.load(0, ln.lane, buf[0].kw, buf[0].vw, buf[0].vm);
+  if constexpr (KB < 16) {
+#pragma unroll
+    for (int f = 0; f < R; ++f) kmr[f] = f < nk ? src.kmeta(f, ln.lane) : u4_t{0, 0, 0, 0};
+  }
+  auto step = [&](auto J, int k) {
+    constexpr int j = decltype(J)::value;
+    const int e = STACK ? k % R : 0;  // slot of this group in its stack
+    if constexpr (KB < 16) {
+      if (e == 0) {
+#pragma unroll
+        for (int f = 0; f < R; ++f) *(u4_t*)(kmeta + 256 * f + 4 * ln.lane) = kmr[f];
+      }
+    }
+    if constexpr (VB < 16) *(u4_t*)(vmeta + 4 * ln.lane) = buf[j].vm;
+    wave_sync_lds();
+    if (k + 1 < nk) src.load(k + 1, ln.lane, buf[j ^ 1].kw, buf[j ^ 1].vw, buf[j ^ 1].vm);
+    if constexpr (KB < 16) {
+      if (k + 1 < nk && (k + 1) % R == 0) {
+#pragma unroll
+        for (int f = 0; f < R; ++f) kmr[f] = k + 1 + f < nk ? src.kmeta(k + 1 + f, ln.lane) : u4_t{0, 0, 0, 0};
+      }
+    }
+    int srcl = -1;  // the lane holding this lane's scores: same row, column of slot e
+    if constexpr (STACK) {
+      if (e == 0) beta = k_operands(ln, kmeta + 256 * (ln.col_ok ? ln.slot : 0), bh, bl);
+      srcl = ((ln.lane & 48) | (ln.gcol + ln.g * e)) * 4;
+    }
+    process_group<KB, VB, KTOK, NS, false, VPAGE>(buf[j].kw, buf[j].vw, kmeta, vmeta, GS, bh, bl, beta, srcl, ln,
+                                                  acc);
+    wave_sync_lds();
+  };
+  for (int k = 0; k < nk; k += 2) {
+    step(std::integral_constant<int, 0>{}, k);
+    if (k + 1 < nk) step(std::integral_constant<int, 1>{}, k + 1);
+  }
+}
+
+// Contiguous streams: one workgroup per (split, KV head, request).
+template <int KB, int VB, bool KTOK, int NS>
+__global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
+  constexpr int R = (KB < 16 && !KTOK) ? NS : 1;
+  __shared__ SplitSmem<R> sm;
+  const LayerGeom& g = a.geo;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
+  int L = a.seq_lens[r];
+  if (L < 0) L = 0;
+  if (L > g.max_tokens) L = g.max_tokens;
+  const int nq = L / GS;
+  const int T = L - nq * GS;
+  const int nvg = nq + (T > 0);
+  const int g0 = split * a.groups_per_split;
+  const int g1 = min(g0 + a.groups_per_split, nvg);
+  const uint8_t* stream = g.base + (size_t)(r * g.hkv + h) * g.stream_bytes;
+
+  Lane ln;
+  Acc acc;
+  setup_lane<NS, KTOK && KB < 16>(a, r, h, sm.q, ln, acc);
+  float* kmeta = &sm.kmeta[wave][0][0];
+  float* vmeta = sm.vmeta[wave];
+
+  // the fp16 tail first, in true units, by the wave that owns it
+  if (T > 0 && nq >= g0 && nq < g1 && ((nq - g0) & (kWaves - 1)) == wave) {
     const uint8_t* rec = stream + g.tail_offset;
     uint32_t kw[32], vw[32];
     load_codes<16>(rec, ln.lane, kw);
@@ -399,124 +632,109 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // ----------------------------- the wave's packed groups: g0 + wave + 4 k
-  // Each loop is unrolled by its two register buffers so that every buffer
-  // index is static (no register copies).
+  // the wave's packed groups: g0 + wave + 4 k
   const int first = g0 + wave;
   const int qend = min(g1, nq);
   const int nk = first < qend ? (qend - first + kWaves - 1) / kWaves : 0;
-  const uint32_t rb = (uint32_t)g.record_bytes;
-  const RecordParts parts = record_parts(KB, VB);
-  auto rec_of = [&](int k) { return stream + (size_t)(first + kWaves * k) * rb; };
-  auto kmeta_of = [&](int k) { return *(const u4_t*)(rec_of(k) + parts.kmeta + ln.lane * 16); };
-  if (nk > 0) {
-    // One group at a time, one group loading ahead.
-    struct Buf {
-      uint32_t kw[NKW];
-      uint32_t vw[NVW];
-      u4_t vm;
-    };
-    Buf buf[2];
-    u4_t kmr[KM];
+  StreamSrc<KB, VB> src;
+  src.first = stream + (size_t)first * g.record_bytes;
+  src.stride = (uint32_t)(kWaves * g.record_bytes);
+  src.parts = record_parts(KB, VB);
+  run_groups<KB, VB, KTOK, NS, R>(src, nk, kmeta, vmeta, ln, acc);
+  finish<VB, NS>(a, r, h, split, wave, sm, ln, acc);
+}
+
+// Paged pool: the splits of a request cover its INT2 groups first, then its
+// INT4 page pairs, each split of one kind only (TriAxialKV page, "Facts": the
+// page table puts INT2 pages first, so flash-decoding splits are
+// bitwidth-homogeneous; their partials merge by log-sum-exp).
+template <int NS>
+__device__ __forceinline__ void paged_int2_split(const DecodeArgs& a, SplitSmem<NS>& sm, int r, int h, int split,
+                                                 int g0, int g1, const int32_t* table) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Lane ln;
+  Acc acc;
+  setup_lane<NS, false>(a, r, h, sm.q, ln, acc);
+  const int first = g0 + wave;
+  const int nk = first < g1 ? (g1 - first + kWaves - 1) / kWaves : 0;
+  Int2Src src;
+  src.base = a.geo.base + (size_t)h * INT2_RECORD;
+  src.page_bytes = a.pg.int2_page_bytes;
+  src.ids = ln.lane < nk ? table[2 * (first + kWaves * ln.lane)] : 0;
+  run_groups<2, 2, false, NS, NS>(src, nk, &sm.kmeta[wave][0][0], sm.vmeta[wave], ln, acc);
+  finish<2, NS>(a, r, h, split, wave, sm, ln, acc);
+}
+
+template <int NS>
+__device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<NS>& sm, int r, int h, int split,
+                                                 int g0, int g1, int n4, const int32_t* table) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Lane ln;
+  Acc acc;
+  setup_lane<NS, true>(a, r, h, sm.q, ln, acc);
+  float* kmeta = &sm.kmeta[wave][0][0];
+  float* vmeta = sm.vmeta[wave];
+  const int full = n4 / GS;  // page pairs holding 32 tokens
+  const int np = (n4 + PAGE_TOKENS - 1) / PAGE_TOKENS;
+  Int4Src src;
+  src.base = a.geo.base + a.pg.int4_offset + (size_t)h * INT4_HEAD;
+  src.page_bytes = a.pg.int4_page_bytes;
+  auto region = [&](int e) { return e < np ? table[e] - a.pg.int2_pages : 0; };
+
+  // the last, partly filled pair first, by the wave that owns it
+  const int pg = full;
+  if (pg < (n4 + GS - 1) / GS && pg >= g0 && pg < g1 && ((pg - g0) & (kWaves - 1)) == wave) {
+    const int ntok = n4 - GS * pg;
+    src.ida = region(2 * pg);
+    src.idb = ntok > PAGE_TOKENS ? region(2 * pg + 1) : src.ida;
+    uint32_t kw[8], vw[8];
+    u4_t vm;
+    src.load(0, ln.lane, kw, vw, vm);
+    u4_t km = src.kmeta(0, ln.lane);
+    // slots at or past ntok hold no token: zero their meta (scores are masked
+    // to -inf and value codes to 0 by the group's tail handling)
+    const int j0 = 16 * (ln.lane & 1) + 4 * (((ln.lane & 31) >> 1) & 3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (j0 + i >= ntok) {
+        vm[i] = 0u;
+        km[i] = 0u;
+      }
+    }
+    *(u4_t*)(kmeta + 4 * ln.lane) = km;
+    *(u4_t*)(vmeta + 4 * ln.lane) = vm;
+    wave_sync_lds();
     h8_t bh[4], bl[4];
-    float beta = 0.f;
-    if constexpr (!STACK) q_operands(ln, bh, bl);
-    auto issue = [&](Buf& bf, int k) {
-      const uint8_t* rec = rec_of(k);
-      load_codes<KB>(rec, ln.lane, bf.kw);
-      load_codes<VB>(rec + parts.vcode, ln.lane, bf.vw);
-      if constexpr (VB < 16) bf.vm = *(const u4_t*)(rec + parts.vmeta + ln.lane * 16);
-    };
-    issue(buf[0], 0);
-    if constexpr (KB < 16) {
-#pragma unroll
-      for (int f = 0; f < KM; ++f) kmr[f] = f < nk ? kmeta_of(f) : u4_t{0, 0, 0, 0};
-    }
-    auto step = [&](auto J, int k) {
-      constexpr int j = decltype(J)::value;
-      const int e = STACK ? k % R : 0;  // slot of this group in its stack
-      if constexpr (KB < 16) {
-        if (e == 0) {
-#pragma unroll
-          for (int f = 0; f < KM; ++f) *(u4_t*)(kmeta + 256 * f + 4 * ln.lane) = kmr[f];
-        }
-      }
-      if constexpr (VB < 16) *(u4_t*)(vmeta + 4 * ln.lane) = buf[j].vm;
-      wave_sync_lds();
-      if (k + 1 < nk) issue(buf[j ^ 1], k + 1);
-      if constexpr (KB < 16) {
-        if (k + 1 < nk && (k + 1) % KM == 0) {
-#pragma unroll
-          for (int f = 0; f < KM; ++f) kmr[f] = k + 1 + f < nk ? kmeta_of(k + 1 + f) : u4_t{0, 0, 0, 0};
-        }
-      }
-      int src = -1;
-      if constexpr (STACK) {
-        if (e == 0) beta = k_operands(ln, kmeta + 256 * (ln.col_ok ? ln.slot : 0), bh, bl);
-        src = ((ln.lane & 48) | (ln.gcol + G * e)) * 4;
-      }
-      process_group<KB, VB, KTOK, NS, false>(buf[j].kw, buf[j].vw, kmeta, vmeta, GS, bh, bl, beta, src, ln, acc);
-      wave_sync_lds();
-    };
-    for (int k = 0; k < nk; k += 2) {
-      step(std::integral_constant<int, 0>{}, k);
-      if (k + 1 < nk) step(std::integral_constant<int, 1>{}, k + 1);
-    }
+    q_operands(ln, bh, bl);
+    process_group<4, 4, true, NS, true, true>(kw, vw, kmeta, vmeta, ntok, bh, bl, 0.f, -1, ln, acc);
+    wave_sync_lds();
   }
 
-  // ------------------------------------------- this wave's result into LDS
-  const float l = sum_lane_groups(acc.lpart);
-  const float vmul = code_scale<VB>();
-#pragma unroll
-  for (int pass = 0; pass < 4 / NS; ++pass) {
-    const float z = sum_lane_groups(acc.zpart[pass]);
-    const int n = pass * NS + ln.slot;
-    if (ln.col_ok) {
-#pragma unroll
-      for (int u = 2 * pass * NS; u < 2 * (pass + 1) * NS; ++u) {
-        if (u / 2 != n) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s_o[wave][ln.gcol][16 * u + 4 * ln.la + i] = fmaf(fmaf(acc.ol[u][i], kLoDown, acc.o[u][i]), vmul, z);
-      }
-    }
-  }
-  if (ln.lane < G) {
-    s_ml[wave][0][ln.lane] = acc.m;
-    s_ml[wave][1][ln.lane] = l;
-  }
-  __syncthreads();
-  // ------------------------------------ combine the four waves and write
-  for (int idx = tid; idx < G * D; idx += blockDim.x) {
-    const int gg = idx >> 7, c = idx & 127;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][0][gg]);
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_ml[w][0][gg];
-        if (mw == -INFINITY) continue;
-        const float e = __builtin_amdgcn_exp2f(mw - M);
-        num = fmaf(e, s_o[w][gg][c], num);
-        den = fmaf(e, s_ml[w][1][gg], den);
-      }
-    }
-    const float o = den > 0.f ? num / den : 0.f;
-    const float lse = den > 0.f ? (M + __log2f(den)) * 0.69314718055994531f : -INFINITY;
-    const size_t qrow = (size_t)r * g.hq + h * G + gg;
-    if (a.splits == 1) {  // the only split: final output
-      if (a.out_f32)
-        ((float*)a.out)[qrow * D + c] = o;
-      else
-        ((_Float16*)a.out)[qrow * D + c] = (_Float16)o;
-      if (c == 0 && a.lse_out) a.lse_out[qrow] = lse;
-    } else {
-      const size_t row = qrow * a.splits + split;
-      a.part_o[row * D + c] = o;
-      if (c == 0) a.part_lse[row] = lse;
-    }
+  const int first = g0 + wave;
+  const int qend = min(g1, full);
+  const int nk = first < qend ? (qend - first + kWaves - 1) / kWaves : 0;
+  const int gi = first + kWaves * ln.lane;
+  src.ida = ln.lane < nk ? region(2 * gi) : 0;
+  src.idb = ln.lane < nk ? region(2 * gi + 1) : 0;
+  run_groups<4, 4, true, NS, 1>(src, nk, kmeta, vmeta, ln, acc);
+  finish<4, NS>(a, r, h, split, wave, sm, ln, acc);
+}
+
+template <int NS>
+__global__ __launch_bounds__(256, 2) void paged_split_kernel(DecodeArgs a) {
+  __shared__ SplitSmem<NS> sm;
+  const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
+  const int n2 = max(a.pg.int2_len[r], 0), n4 = max(a.pg.int4_len[r], 0);
+  const int gps = a.groups_per_split;
+  const int n2g = n2 / GS, n4g = (n4 + GS - 1) / GS;
+  const int s2 = (n2g + gps - 1) / gps;  // splits of the INT2 part
+  const int32_t* table = a.pg.table + (size_t)r * a.pg.max_pages;
+  if (split < s2) {
+    const int g0 = split * gps;
+    paged_int2_split<NS>(a, sm, r, h, split, g0, min(g0 + gps, n2g), table);
+  } else {
+    const int g0 = (split - s2) * gps;
+    paged_int4_split<NS>(a, sm, r, h, split, g0, min(g0 + gps, n4g), n4, table + n2 / PAGE_TOKENS);
   }
 }
 
@@ -548,6 +766,14 @@ hipError_t launch_k(const DecodeArgs& a, int batch, hipStream_t s, const EventPa
 }
 
 }  // namespace
+
+hipError_t launch_decode_paged(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
+  const dim3 grid(a.splits, a.geo.hkv, batch), block(256);
+  const int per = 16 / a.geo.g;
+  if (per >= 4) return launch_timed(paged_split_kernel<4>, grid, block, s, ev, a);
+  if (per >= 2) return launch_timed(paged_split_kernel<2>, grid, block, s, ev, a);
+  return launch_timed(paged_split_kernel<1>, grid, block, s, ev, a);
+}
 
 hipError_t launch_decode_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
   switch (a.geo.kb) {

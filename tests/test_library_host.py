@@ -161,3 +161,48 @@ def test_auto_split_count():
     s = kvq.num_splits(plan, 0, 64, 2048)
     assert 1 <= s <= 64
     assert kvq.workspace_bytes(plan, 64, 2048) == 64 * 32 * s * 129 * 4
+
+
+def _paged_plan():
+    return kvq.plan_layers(kvq.make_shape(32, 8, 4, page_tokens=16, int2_pages=64, int4_pages=64), [(2, 2, 0, 1)])
+
+
+def test_paged_argument_errors(lib):
+    paged = _paged_plan()
+    contig = kvq.plan_layers(kvq.make_shape(32, 8, 4, max_tokens=256), [(8, 4)])
+    f = ctypes.c_void_p(0x1000)
+    pages = kvq.make_pages(_Fake(), 128, _Fake(), _Fake())
+
+    def dec(plan, pg, max_seq_len=64, splits=0):
+        return lib.kvq_decode_attention(ctypes.byref(plan), 0, f, f, None, 2, max_seq_len, ctypes.c_float(0.088), f, 0,
+                                        None, f, 1 << 30, splits, ctypes.byref(pg) if pg else None, None)
+
+    assert dec(paged, None) == kvq.ERR_INVALID_ARG  # a paged plan needs pages
+    assert dec(contig, pages) == kvq.ERR_INVALID_ARG  # pages for a contiguous plan
+    assert dec(paged, kvq.make_pages(_Fake(), 128, None, _Fake())) == kvq.ERR_INVALID_ARG
+    assert dec(paged, kvq.make_pages(_Fake(), 0, _Fake(), _Fake())) == kvq.ERR_INVALID_ARG
+    assert dec(paged, pages, max_seq_len=128 * 16 + 1) == kvq.ERR_CAPACITY
+    assert dec(paged, pages, splits=1) == kvq.ERR_INVALID_ARG  # one kind per split: at least 2
+    big = kvq.make_pages(_Fake(), 4096, _Fake(), _Fake())
+    assert dec(paged, big, max_seq_len=32 * 300, splits=2) == kvq.ERR_INVALID_ARG  # 300 groups in a split
+    assert "256" in lib.kvq_last_error().decode()
+    P = ctypes.byref(paged)
+    assert lib.kvq_quantize_append(P, 0, f, f, f, None, 2, 3, None, None) == kvq.ERR_INVALID_ARG
+    assert lib.kvq_quantize_append(P, 0, f, f, f, None, 2, 128 * 16 + 1, ctypes.byref(pages), None) == \
+        kvq.ERR_CAPACITY
+    assert lib.kvq_dequantize(P, 0, f, None, 2, 30, f, f, None, None) == kvq.ERR_INVALID_ARG
+    assert lib.kvq_dequantize(P, 0, f, None, 2, 128 * 16 + 1, f, f, ctypes.byref(pages), None) == kvq.ERR_CAPACITY
+
+
+@pytest.mark.parametrize("batch,max_seq_len", [(16, 32768), (1, 32768), (64, 100), (4, 1), (2, 0)])
+def test_paged_auto_splits_hold_the_limits(batch, max_seq_len):
+    """Automatic paged split count: at least 2, and ceil(groups / (splits - 1)) <= 256."""
+    plan = kvq.plan_layers(kvq.make_shape(32, 8, 64, page_tokens=16, int2_pages=64, int4_pages=64), [(2, 2, 0, 1)])
+    s = kvq.num_splits(plan, 0, batch, max_seq_len)
+    groups = (max_seq_len + 31) // 32
+    if groups == 0:
+        assert s >= 1
+        return
+    assert 2 <= s <= 1024
+    assert -(-groups // (s - 1)) <= 256
+    assert kvq.workspace_bytes(plan, batch, max_seq_len) == batch * 32 * s * 129 * 4
