@@ -82,17 +82,21 @@ def capacity(w):
 class Workload:
     """A planned, prefilled cache on the GPU plus the inputs of every decode step."""
 
-    def __init__(self, name, seed=0, device="cuda", num_splits=0, gen_chunk=8):
+    def __init__(self, name, seed=0, device="cuda", num_splits=0, gen_chunk=8, layers=None):
+        """layers: indices of the workload's layers to build (default all); a subset keeps every
+        layer's shapes, data and launches, and is used by the full-size parity tests."""
         import torch
 
         import layer_wise_mixed_amd as kvq
 
         self.name, self.seed, self.kvq = name, seed, kvq
         w = self.w = WORKLOADS[name]
-        self.L, self.B, self.Hq, self.Hkv = w["layers"], w["batch"], w["hq"], w["hkv"]
+        self.layer_ids = list(range(w["layers"])) if layers is None else list(layers)
+        self.L, self.B, self.Hq, self.Hkv = len(self.layer_ids), w["batch"], w["hq"], w["hkv"]
         self.P, self.C = w["prefill"], w["cycle"]
         self.cap = capacity(w)
-        self.cfg = w["map"](seed)
+        full_map = w["map"](seed)
+        self.cfg = [full_map[i] for i in self.layer_ids]
         self.outliers = w["outliers"]
         self.shape = kvq.make_shape(self.Hq, self.Hkv, self.B, max_tokens=self.cap)
         self.plan = kvq.plan_layers(self.shape, self.cfg)
@@ -100,23 +104,23 @@ class Workload:
         self.scale = 1.0 / math.sqrt(128.0)
         self.num_splits = num_splits
         zeros = torch.zeros(self.B, dtype=torch.int32, device=device)
-        for l in range(self.L):  # prefill, a few requests at a time
+        for l, li in enumerate(self.layer_ids):  # prefill, a few requests at a time
             for r0 in range(0, self.B, gen_chunk):
                 rs = range(r0, min(self.B, r0 + gen_chunk))
-                k = self.keys(l, rs, 0, self.P, device)
-                v = syn.values_fp16(seed, l, rs, range(self.Hkv), 0, self.P, device=device)
+                k = self.keys(li, rs, 0, self.P, device)
+                v = syn.values_fp16(seed, li, rs, range(self.Hkv), 0, self.P, device=device)
                 off = r0 * self.Hkv * self.plan.layers[l].stream_bytes
                 kvq.quantize_append(self.plan, l, self.cache[off:], k, v, zeros[: len(rs)])
                 del k, v
         torch.cuda.synchronize()
         # decode-step inputs: [cycle][batch][heads][1][128] and q [cycle][batch][Hq][128]
         self.k_dec, self.v_dec, self.q = [], [], []
-        for l in range(self.L):
-            k = self.keys(l, range(self.B), self.P, self.C, device)
-            v = syn.values_fp16(seed, l, range(self.B), range(self.Hkv), self.P, self.C, device=device)
+        for li in self.layer_ids:
+            k = self.keys(li, range(self.B), self.P, self.C, device)
+            v = syn.values_fp16(seed, li, range(self.B), range(self.Hkv), self.P, self.C, device=device)
             self.k_dec.append(k.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
             self.v_dec.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
-            qq = syn.queries_steps_fp16(seed, l, self.B, self.Hq, 0, self.C, device=device)
+            qq = syn.queries_steps_fp16(seed, li, self.B, self.Hq, 0, self.C, device=device)
             self.q.append(qq.permute(2, 0, 1, 3).contiguous())
         self.lens_base = torch.full((self.B,), self.P, dtype=torch.int32, device=device)
         self.lens_before = self.lens_base.clone()
@@ -167,14 +171,15 @@ class PagedWorkload:
 
     PAGE = 16
 
-    def __init__(self, name, seed=0, device="cuda", num_splits=0):
+    def __init__(self, name, seed=0, device="cuda", num_splits=0, layers=None):
         import torch
 
         import layer_wise_mixed_amd as kvq
 
         self.name, self.seed, self.kvq = name, seed, kvq
         w = self.w = WORKLOADS[name]
-        self.L, self.B, self.Hq, self.Hkv = w["layers"], w["batch"], w["hq"], w["hkv"]
+        self.layer_ids = list(range(w["layers"])) if layers is None else list(layers)
+        self.L, self.B, self.Hq, self.Hkv = len(self.layer_ids), w["batch"], w["hq"], w["hkv"]
         self.P, self.C = w["prefill"], w["cycle"]
         self.outliers = w["outliers"]
         self.scale = 1.0 / math.sqrt(128.0)
@@ -203,22 +208,22 @@ class PagedWorkload:
         zero = torch.zeros(self.B, dtype=torch.int32, device=device)
         add2 = torch.full((self.B,), self.n2, dtype=torch.int32, device=device)
         orders = [torch.tensor(self._prompt_order(r), dtype=torch.int64, device=device) for r in range(self.B)]
-        for l in range(self.L):  # prefill one request at a time: INT2 runs first, then the rest
+        for l, li in enumerate(self.layer_ids):  # prefill one request at a time: INT2 runs first, then the rest
             for r in range(self.B):
                 order = orders[r]
-                k = self.keys(l, [r], 0, self.P, device).index_select(2, order)
-                v = syn.values_fp16(seed, l, [r], range(self.Hkv), 0, self.P, device=device).index_select(2, order)
+                k = self.keys(li, [r], 0, self.P, device).index_select(2, order)
+                v = syn.values_fp16(seed, li, [r], range(self.Hkv), 0, self.P, device=device).index_select(2, order)
                 pages = kvq.make_pages(self.table[r], self.max_pages, zero[r:], zero[r:], add2[r:])
                 kvq.quantize_append(self.plan, l, self.cache, k, v, None, pages)
                 del k, v
         torch.cuda.synchronize()
         self.k_dec, self.v_dec, self.q = [], [], []
-        for l in range(self.L):
-            k = self.keys(l, range(self.B), self.P, self.C, device)
-            v = syn.values_fp16(seed, l, range(self.B), range(self.Hkv), self.P, self.C, device=device)
+        for li in self.layer_ids:
+            k = self.keys(li, range(self.B), self.P, self.C, device)
+            v = syn.values_fp16(seed, li, range(self.B), range(self.Hkv), self.P, self.C, device=device)
             self.k_dec.append(k.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
             self.v_dec.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
-            qq = syn.queries_steps_fp16(seed, l, self.B, self.Hq, 0, self.C, device=device)
+            qq = syn.queries_steps_fp16(seed, li, self.B, self.Hq, 0, self.C, device=device)
             self.q.append(qq.permute(2, 0, 1, 3).contiguous())
         self.n2_dev = torch.full((self.B,), self.n2, dtype=torch.int32, device=device)
         self.n4_base = torch.full((self.B,), self.P - self.n2, dtype=torch.int32, device=device)
@@ -305,7 +310,7 @@ def cpu_baseline_paged(wl, max_seconds=20.0):
 
     n4 = wl.P - wl.n2 + wl.C  # INT4 tokens at the last step of the cycle
     G = wl.Hq // wl.Hkv
-    layer = 0
+    layer = wl.layer_ids[0]
     n_streams = min(wl.B * wl.Hkv, 16)
     pool = np.zeros(oracle.paged_pool_bytes(wl.Hkv, wl.int2_pages, wl.int4_pages), np.uint8)
     tables = wl.table.cpu().numpy()
@@ -350,8 +355,8 @@ def cpu_baseline(wl, max_seconds=20.0):
 
     L = wl.P + wl.C  # the last step of the cycle
     G = wl.Hq // wl.Hkv
-    layer = 0
-    lp = wl.plan.layers[layer]
+    layer = wl.layer_ids[0]
+    lp = wl.plan.layers[0]
     kb, vb, kt = lp.k_bits, lp.v_bits, lp.k_axis == 1
     cap_groups = wl.cap // 32
     stride = oracle.stream_bytes(kb, vb, cap_groups)

@@ -38,6 +38,7 @@
 
 #include "kvq_internal.h"
 
+
 namespace kvq {
 namespace {
 
@@ -111,15 +112,22 @@ __device__ inline void load_codes(const uint8_t* blk, int lane, uint32_t* w) {
   }
 }
 
-// element i of (hi, lo): the fp16 rounding of x, and what it missed scaled by
-// 2^11 (exact), so the low part stays in the normal fp16 range whenever x does.
+// elements i, i+1 of (hi, lo): an fp16 rounding of x, and what it missed,
+// scaled by 2^11, rounded to fp16 (the low part stays in the normal fp16 range
+// whenever x does), so hi + lo / 2^11 keeps ~21 significant bits of x. The
+// high part is one packed round-toward-zero conversion, an operation the
+// compiler cannot re-form from the product behind x: were it to round the
+// product once in one place (a fused multiply-round) and twice in another, the
+// two parts would disagree by an fp16 ulp.
 constexpr float kLoUp = 2048.0f;
 constexpr float kLoDown = 1.0f / 2048.0f;
 
-__device__ inline void set_hi_lo(h8_t& hi, h8_t& lo, int i, float x) {
-  const _Float16 h = (_Float16)x;
-  hi[i] = h;
-  lo[i] = (_Float16)((x - (float)h) * kLoUp);
+__device__ inline void set_hi_lo2(h8_t& hi, h8_t& lo, int i, float x0, float x1) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+  hi[i] = h[0];
+  hi[i + 1] = h[1];
+  lo[i] = (_Float16)((x0 - (float)h[0]) * kLoUp);
+  lo[i + 1] = (_Float16)((x1 - (float)h[1]) * kLoUp);
 }
 
 __device__ inline void wave_sync_lds() {
@@ -162,7 +170,7 @@ __device__ inline void q_operands(const Lane& ln, h8_t* qh, h8_t* ql) {
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) set_hi_lo(qh[s], ql[s], i, ln.qv[32 * s + i]);
+    for (int i = 0; i < 8; i += 2) set_hi_lo2(qh[s], ql[s], i, ln.qv[32 * s + i], ln.qv[32 * s + i + 1]);
 }
 
 // B operand q' * scale_k of per-channel keys for the group of this lane's slot,
@@ -173,10 +181,10 @@ __device__ inline float k_operands(const Lane& ln, const float* kmeta, h8_t* bh,
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float q = ln.qv[32 * s + i];
-      set_hi_lo(bh[s], bl[s], i, q * ks[8 * s + i]);
-      beta = fmaf(q, ks[128 + 8 * s + i], beta);
+    for (int i = 0; i < 8; i += 2) {
+      const float q0 = ln.qv[32 * s + i], q1 = ln.qv[32 * s + i + 1];
+      set_hi_lo2(bh[s], bl[s], i, q0 * ks[8 * s + i], q1 * ks[8 * s + i + 1]);
+      beta = fmaf(q1, ks[128 + 8 * s + i + 1], fmaf(q0, ks[128 + 8 * s + i], beta));
     }
   return sum_lane_groups(beta);
 }
@@ -297,15 +305,15 @@ __device__ __forceinline__ void group_pv(const uint32_t* vw, const float* vmeta,
     h8_t vh, vl;
     if constexpr (VB == 16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) set_hi_lo(vh, vl, i, p[i]);
+      for (int i = 0; i < 8; i += 2) set_hi_lo2(vh, vl, i, p[i], p[i + 1]);
     } else {
       const int n = ln.col_ok ? pass * NS + ln.slot : 0;
       const float* vs = vmeta + 32 * n + 8 * ln.la;
       float zp = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        set_hi_lo(vh, vl, i, p[i] * vs[i]);
-        zp = fmaf(p[i], vs[128 + i], zp);
+      for (int i = 0; i < 8; i += 2) {
+        set_hi_lo2(vh, vl, i, p[i] * vs[i], p[i + 1] * vs[i + 1]);
+        zp = fmaf(p[i + 1], vs[128 + i + 1], fmaf(p[i], vs[128 + i], zp));
       }
       acc.zpart[pass] += zp;
     }

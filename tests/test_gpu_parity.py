@@ -19,6 +19,18 @@ MAX_ABS = 2e-3
 LSE_ABS = 1e-4
 
 
+def lse_tolerance(q_fp16, kdeq, scale):
+    """Per-row bound on |lse - lse_oracle|: 1e-4 plus 2^-19 times the largest sum of absolute
+    products max_j sum_c |q_c k_jc| * scale. The split pass forms scores in fp32 from ~22-bit
+    products, and folding per-channel scales and zero points cancels terms of that size, so
+    its score error is a small multiple of 2^-22 of that sum; 2^-19 leaves a factor 8."""
+    q = np.abs(np.asarray(q_fp16, dtype=np.float64).reshape(-1, 128))
+    k = np.abs(np.asarray(kdeq, dtype=np.float64).reshape(-1, 128))
+    if k.shape[0] == 0:
+        return np.full(q.shape[0], LSE_ABS)
+    return LSE_ABS + 2.0 ** -19 * (q @ k.T).max(axis=1) * scale
+
+
 class Case:
     """A small cache built request by request (ragged lengths) with one append each."""
 
