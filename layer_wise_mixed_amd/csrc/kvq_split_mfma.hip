@@ -345,17 +345,25 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
 
 // Every member is a multiple of 16 bytes long, so with the struct aligned
 // each member is too (LDS reads of q', meta and results stay 16 bytes wide).
+// The meta staging of the group loop and the per-wave results of the combine
+// share storage: the combine starts after a barrier that ends every loop.
 template <int R>
 struct alignas(16) SplitSmem {
-  float kmeta[kWaves][R][256];  // per wave: the key meta of up to R groups
-  float vmeta[kWaves][256];     // per wave: the value meta of the current group
-  float o[kWaves][kMaxG][D];    // per wave: its result, for the combine
+  struct Loop {
+    float kmeta[kWaves][R][256];  // per wave: the key meta of up to R groups
+    float vmeta[kWaves][256];     // per wave: the value meta of the current group
+  };
+  union {
+    Loop loop;
+    float o[kWaves][kMaxG][D];  // per wave: its result, for the combine
+  };
   float ml[kWaves][2][kMaxG];
-  float q[kMaxG][D];            // q' of the G query rows
+  float q[kMaxG][D];  // q' of the G query rows (every wave writes the same values)
 };
 
 // The lane's roles, q' = q * softmax_scale * log2(e) of the G rows into LDS,
-// and (per-token keys) the sums of q' over each 32-channel group.
+// and (per-token keys) the sums of q' over each 32-channel group. Every wave
+// writes all of q' (the same values), so no wave waits for another.
 template <int NS, bool QN>
 __device__ __forceinline__ void setup_lane(const DecodeArgs& a, int r, int h, float (*s_q)[D], Lane& ln, Acc& acc) {
   const int tid = threadIdx.x;
@@ -367,10 +375,21 @@ __device__ __forceinline__ void setup_lane(const DecodeArgs& a, int r, int h, fl
   ln.gcol = c16 % G;
   ln.slot = c16 / G;
   ln.col_ok = ln.slot < NS;
-  for (int idx = tid; idx < G * D; idx += blockDim.x)
-    s_q[idx >> 7][idx & 127] = (float)__builtin_bit_cast(_Float16, a.q[((size_t)r * a.geo.hq + h * G) * D + idx]) *
-                               a.scale_log2;
-  __syncthreads();
+  const uint16_t* qg = a.q + ((size_t)r * a.geo.hq + h * G) * D;
+  for (int c = ln.lane; c < G * (D / 8); c += 64) {  // 8 values a lane at a time
+    const u4_t w = *(const u4_t*)(qg + 8 * c);
+    const h8_t x = __builtin_bit_cast(h8_t, w);
+    float* dst = &s_q[c >> 4][8 * (c & 15)];
+    f4_t lo4, hi4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo4[i] = (float)x[i] * a.scale_log2;
+      hi4[i] = (float)x[4 + i] * a.scale_log2;
+    }
+    *(f4_t*)dst = lo4;
+    *(f4_t*)(dst + 4) = hi4;
+  }
+  wave_sync_lds();
   ln.qv = &s_q[ln.gcol][8 * ln.la];
   if constexpr (QN) {
 #pragma unroll
@@ -403,6 +422,7 @@ __device__ __forceinline__ void finish(const DecodeArgs& a, int r, int h, int sp
   const int G = a.geo.g;
   const float l = sum_lane_groups(acc.lpart);
   const float vmul = code_scale<VB>();
+  __syncthreads();  // every wave is out of its group loop: sm.o may reuse the meta staging
 #pragma unroll
   for (int pass = 0; pass < 4 / NS; ++pass) {
     const float z = sum_lane_groups(acc.zpart[pass]);
@@ -479,14 +499,14 @@ struct StreamSrc {
   uint32_t stride;       // kWaves records
   RecordParts parts;
   static constexpr bool kVPage = false;
-  __device__ const uint8_t* rec(int k) const { return first + (size_t)k * stride; }
-  __device__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
+  __device__ __forceinline__ const uint8_t* rec(int k) const { return first + (size_t)k * stride; }
+  __device__ __forceinline__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
     const uint8_t* r = rec(k);
     load_codes<KB>(r, lane, kw);
     load_codes<VB>(r + parts.vcode, lane, vw);
     if constexpr (VB < 16) vm = *(const u4_t*)(r + parts.vmeta + lane * 16);
   }
-  __device__ u4_t kmeta(int k, int lane) const { return *(const u4_t*)(rec(k) + parts.kmeta + lane * 16); }
+  __device__ __forceinline__ u4_t kmeta(int k, int lane) const { return *(const u4_t*)(rec(k) + parts.kmeta + lane * 16); }
 };
 
 // INT2 groups of a paged request: the K2V2 record of one KV head in the page
@@ -497,16 +517,16 @@ struct Int2Src {
   uint64_t page_bytes;
   int ids;
   static constexpr bool kVPage = false;
-  __device__ const uint8_t* rec(int k) const {
+  __device__ __forceinline__ const uint8_t* rec(int k) const {
     return base + (size_t)__builtin_amdgcn_readlane(ids, k) * page_bytes;
   }
-  __device__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
+  __device__ __forceinline__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
     const uint8_t* r = rec(k);
     load_codes<2>(r, lane, kw);
     load_codes<2>(r + 1024, lane, vw);
     vm = *(const u4_t*)(r + 3072 + lane * 16);
   }
-  __device__ u4_t kmeta(int k, int lane) const { return *(const u4_t*)(rec(k) + 2048 + lane * 16); }
+  __device__ __forceinline__ u4_t kmeta(int k, int lane) const { return *(const u4_t*)(rec(k) + 2048 + lane * 16); }
 };
 
 // INT4 page pairs of a paged request: group i is the pages of table entries
@@ -517,8 +537,8 @@ struct Int4Src {
   uint64_t page_bytes;
   int ida, idb;
   static constexpr bool kVPage = true;
-  __device__ const uint8_t* page(int id) const { return base + (size_t)id * page_bytes; }
-  __device__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
+  __device__ __forceinline__ const uint8_t* page(int id) const { return base + (size_t)id * page_bytes; }
+  __device__ __forceinline__ void load(int k, int lane, uint32_t* kw, uint32_t* vw, u4_t& vm) const {
     const uint8_t* pa = page(__builtin_amdgcn_readlane(ida, k));
     const uint8_t* pb = page(__builtin_amdgcn_readlane(idb, k));
     load_codes<2>(pa, lane, kw);  // one 16-byte row per page: key words 0..3 and 4..7
@@ -530,10 +550,10 @@ struct Int4Src {
   // lane l's 16 bytes of a record's per-token meta (record floats 4l .. 4l+3)
   // come from page l % 2: scales for l < 32, zeros after, channel group
   // (l % 32) / 8, slots 4 ((l % 8) / 2) + 0..3
-  __device__ static const uint8_t* meta_site(const uint8_t* pa, const uint8_t* pb, int lane) {
+  __device__ __forceinline__ static const uint8_t* meta_site(const uint8_t* pa, const uint8_t* pb, int lane) {
     return ((lane & 1) ? pb : pa) + (lane >> 5) * 256 + ((lane & 31) >> 1) * 16;
   }
-  __device__ u4_t kmeta(int k, int lane) const {
+  __device__ __forceinline__ u4_t kmeta(int k, int lane) const {
     const uint8_t* pa = page(__builtin_amdgcn_readlane(ida, k));
     const uint8_t* pb = page(__builtin_amdgcn_readlane(idb, k));
     return *(const u4_t*)(meta_site(pa, pb, lane) + INT4_KMETA);
@@ -542,14 +562,14 @@ struct Int4Src {
 
 // The wave's nk packed groups from `src`, one group loading ahead in a second
 // register buffer; the loop is unrolled by two so every buffer index is
-// static (no register copies).
-template <int KB, int VB, bool KTOK, int NS, int R, class Src>
+// static (no register copies). setup() (the wave's q' setup) runs once the
+// first group's loads are issued, so that the two memory waits overlap.
+template <int KB, int VB, bool KTOK, int NS, int R, class Src, class Setup>
 __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta, float* vmeta, const Lane& ln,
-                                           Acc& acc) {
+                                           Acc& acc, Setup&& setup) {
   constexpr bool STACK = KB < 16 && !KTOK;  // per-channel keys: one B operand for R groups
   constexpr int NKW = 2 * KB, NVW = 2 * VB;
   constexpr bool VPAGE = Src::kVPage;
-  if (nk <= 0) return;
   struct Buf {
     uint32_t kw[NKW];
     uint32_t vw[NVW];
@@ -557,14 +577,19 @@ __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta,
   };
   Buf buf[2];
   u4_t kmr[R];
+  const int lane = threadIdx.x & 63;
+  if (nk > 0) {  // the first group loads while setup() waits on q
+    src.load(0, lane, buf[0].kw, buf[0].vw, buf[0].vm);
+    if constexpr (KB < 16) {
+#pragma unroll
+      for (int f = 0; f < R; ++f) kmr[f] = f < nk ? src.kmeta(f, lane) : u4_t{0, 0, 0, 0};
+    }
+  }
+  setup();
+  if (nk <= 0) return;
   h8_t bh[4], bl[4];
   float beta = 0.f;
   if constexpr (!STACK) q_operands(ln, bh, bl);
-  src.load(0, ln.lane, buf[0].kw, buf[0].vw, buf[0].vm);
-  if constexpr (KB < 16) {
-#pragma unroll
-    for (int f = 0; f < R; ++f) kmr[f] = f < nk ? src.kmeta(f, ln.lane) : u4_t{0, 0, 0, 0};
-  }
   auto step = [&](auto J, int k) {
     constexpr int j = decltype(J)::value;
     const int e = STACK ? k % R : 0;  // slot of this group in its stack
@@ -618,27 +643,8 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
 
   Lane ln;
   Acc acc;
-  setup_lane<NS, KTOK && KB < 16>(a, r, h, sm.q, ln, acc);
-  float* kmeta = &sm.kmeta[wave][0][0];
-  float* vmeta = sm.vmeta[wave];
-
-  // the fp16 tail first, in true units, by the wave that owns it
-  if (T > 0 && nq >= g0 && nq < g1 && ((nq - g0) & (kWaves - 1)) == wave) {
-    const uint8_t* rec = stream + g.tail_offset;
-    uint32_t kw[32], vw[32];
-    load_codes<16>(rec, ln.lane, kw);
-    load_codes<16>(rec + 8192, ln.lane, vw);
-    h8_t th[4], tl[4];
-    q_operands(ln, th, tl);
-    process_group<16, 16, false, NS, true>(kw, vw, kmeta, vmeta, T, th, tl, 0.f, -1, ln, acc);
-    if constexpr (VB < 16) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {  // into the packed groups' units
-        acc.o[u] *= 1.0f / code_scale<VB>();
-        acc.ol[u] *= 1.0f / code_scale<VB>();
-      }
-    }
-  }
+  float* kmeta = &sm.loop.kmeta[wave][0][0];
+  float* vmeta = sm.loop.vmeta[wave];
 
   // the wave's packed groups: g0 + wave + 4 k
   const int first = g0 + wave;
@@ -648,7 +654,34 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   src.first = stream + (size_t)first * g.record_bytes;
   src.stride = (uint32_t)(kWaves * g.record_bytes);
   src.parts = record_parts(KB, VB);
-  run_groups<KB, VB, KTOK, NS, R>(src, nk, kmeta, vmeta, ln, acc);
+  run_groups<KB, VB, KTOK, NS, R>(src, nk, kmeta, vmeta, ln, acc,
+                                  [&] { setup_lane<NS, KTOK && KB < 16>(a, r, h, sm.q, ln, acc); });
+
+  // the fp16 tail last (its registers are free now), by the wave that owns
+  // it, in true units: the accumulators go to true units and back
+  if (T > 0 && nq >= g0 && nq < g1 && ((nq - g0) & (kWaves - 1)) == wave) {
+    const uint8_t* rec = stream + g.tail_offset;
+    uint32_t kw[32], vw[32];
+    load_codes<16>(rec, ln.lane, kw);
+    load_codes<16>(rec + 8192, ln.lane, vw);
+    if constexpr (VB < 16) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.o[u] *= code_scale<VB>();
+        acc.ol[u] *= code_scale<VB>();
+      }
+    }
+    h8_t th[4], tl[4];
+    q_operands(ln, th, tl);
+    process_group<16, 16, false, NS, true>(kw, vw, kmeta, vmeta, T, th, tl, 0.f, -1, ln, acc);
+    if constexpr (VB < 16) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.o[u] *= 1.0f / code_scale<VB>();
+        acc.ol[u] *= 1.0f / code_scale<VB>();
+      }
+    }
+  }
   finish<VB, NS>(a, r, h, split, wave, sm, ln, acc);
 }
 
@@ -660,16 +693,17 @@ template <int NS>
 __device__ __forceinline__ void paged_int2_split(const DecodeArgs& a, SplitSmem<NS>& sm, int r, int h, int split,
                                                  int g0, int g1, const int32_t* table) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   Lane ln;
   Acc acc;
-  setup_lane<NS, false>(a, r, h, sm.q, ln, acc);
   const int first = g0 + wave;
   const int nk = first < g1 ? (g1 - first + kWaves - 1) / kWaves : 0;
   Int2Src src;
   src.base = a.geo.base + (size_t)h * INT2_RECORD;
   src.page_bytes = a.pg.int2_page_bytes;
-  src.ids = ln.lane < nk ? table[2 * (first + kWaves * ln.lane)] : 0;
-  run_groups<2, 2, false, NS, NS>(src, nk, &sm.kmeta[wave][0][0], sm.vmeta[wave], ln, acc);
+  src.ids = lane < nk ? table[2 * (first + kWaves * lane)] : 0;
+  run_groups<2, 2, false, NS, NS>(src, nk, &sm.loop.kmeta[wave][0][0], sm.loop.vmeta[wave], ln, acc,
+                                  [&] { setup_lane<NS, false>(a, r, h, sm.q, ln, acc); });
   finish<2, NS>(a, r, h, split, wave, sm, ln, acc);
 }
 
@@ -677,11 +711,11 @@ template <int NS>
 __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<NS>& sm, int r, int h, int split,
                                                  int g0, int g1, int n4, const int32_t* table) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   Lane ln;
   Acc acc;
-  setup_lane<NS, true>(a, r, h, sm.q, ln, acc);
-  float* kmeta = &sm.kmeta[wave][0][0];
-  float* vmeta = sm.vmeta[wave];
+  float* kmeta = &sm.loop.kmeta[wave][0][0];
+  float* vmeta = sm.loop.vmeta[wave];
   const int full = n4 / GS;  // page pairs holding 32 tokens
   const int np = (n4 + PAGE_TOKENS - 1) / PAGE_TOKENS;
   Int4Src src;
@@ -689,7 +723,15 @@ __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<
   src.page_bytes = a.pg.int4_page_bytes;
   auto region = [&](int e) { return e < np ? table[e] - a.pg.int2_pages : 0; };
 
-  // the last, partly filled pair first, by the wave that owns it
+  const int first = g0 + wave;
+  const int qend = min(g1, full);
+  const int nk = first < qend ? (qend - first + kWaves - 1) / kWaves : 0;
+  const int gi = first + kWaves * lane;
+  src.ida = lane < nk ? region(2 * gi) : 0;
+  src.idb = lane < nk ? region(2 * gi + 1) : 0;
+  run_groups<4, 4, true, NS, 1>(src, nk, kmeta, vmeta, ln, acc, [&] { setup_lane<NS, true>(a, r, h, sm.q, ln, acc); });
+
+  // the last, partly filled pair (same units as the full ones), by its wave
   const int pg = full;
   if (pg < (n4 + GS - 1) / GS && pg >= g0 && pg < g1 && ((pg - g0) & (kWaves - 1)) == wave) {
     const int ntok = n4 - GS * pg;
@@ -697,11 +739,11 @@ __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<
     src.idb = ntok > PAGE_TOKENS ? region(2 * pg + 1) : src.ida;
     uint32_t kw[8], vw[8];
     u4_t vm;
-    src.load(0, ln.lane, kw, vw, vm);
-    u4_t km = src.kmeta(0, ln.lane);
+    src.load(0, lane, kw, vw, vm);
+    u4_t km = src.kmeta(0, lane);
     // slots at or past ntok hold no token: zero their meta (scores are masked
     // to -inf and value codes to 0 by the group's tail handling)
-    const int j0 = 16 * (ln.lane & 1) + 4 * (((ln.lane & 31) >> 1) & 3);
+    const int j0 = 16 * (lane & 1) + 4 * (((lane & 31) >> 1) & 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (j0 + i >= ntok) {
@@ -709,22 +751,14 @@ __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<
         km[i] = 0u;
       }
     }
-    *(u4_t*)(kmeta + 4 * ln.lane) = km;
-    *(u4_t*)(vmeta + 4 * ln.lane) = vm;
+    *(u4_t*)(kmeta + 4 * lane) = km;
+    *(u4_t*)(vmeta + 4 * lane) = vm;
     wave_sync_lds();
     h8_t bh[4], bl[4];
     q_operands(ln, bh, bl);
     process_group<4, 4, true, NS, true, true>(kw, vw, kmeta, vmeta, ntok, bh, bl, 0.f, -1, ln, acc);
     wave_sync_lds();
   }
-
-  const int first = g0 + wave;
-  const int qend = min(g1, full);
-  const int nk = first < qend ? (qend - first + kWaves - 1) / kWaves : 0;
-  const int gi = first + kWaves * ln.lane;
-  src.ida = ln.lane < nk ? region(2 * gi) : 0;
-  src.idb = ln.lane < nk ? region(2 * gi + 1) : 0;
-  run_groups<4, 4, true, NS, 1>(src, nk, kmeta, vmeta, ln, acc);
   finish<4, NS>(a, r, h, split, wave, sm, ln, acc);
 }
 
