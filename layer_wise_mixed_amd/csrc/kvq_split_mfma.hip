@@ -560,6 +560,19 @@ struct Int4Src {
   }
 };
 
+// Issue priority from the wave's progress: 1 until three quarters of its
+// groups are done, then 0. Two workgroups share each CU and the older one's
+// waves win the issue arbitration, so with equal work the younger one used
+// to finish a quarter later and run alone meanwhile; the waves that reach
+// three quarters first now yield until the others get there too.
+__device__ __forceinline__ void progress_priority(int done, int nk) {
+  if (4 * done < 3 * nk) {
+    __builtin_amdgcn_s_setprio(1);
+  } else {
+    __builtin_amdgcn_s_setprio(0);
+  }
+}
+
 // The wave's nk packed groups from `src`, one group loading ahead in a second
 // register buffer; the loop is unrolled by two so every buffer index is
 // static (no register copies). setup() (the wave's q' setup) runs once the
@@ -587,6 +600,7 @@ __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta,
   }
   setup();
   if (nk <= 0) return;
+  progress_priority(0, nk);
   h8_t bh[4], bl[4];
   float beta = 0.f;
   if constexpr (!STACK) q_operands(ln, bh, bl);
@@ -616,6 +630,7 @@ __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta,
     process_group<KB, VB, KTOK, NS, false, VPAGE>(buf[j].kw, buf[j].vw, kmeta, vmeta, GS, bh, bl, beta, srcl, ln,
                                                   acc);
     wave_sync_lds();
+    progress_priority(k + 1, nk);
   };
   for (int k = 0; k < nk; k += 2) {
     step(std::integral_constant<int, 0>{}, k);
