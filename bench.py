@@ -82,9 +82,11 @@ def capacity(w):
 class Workload:
     """A planned, prefilled cache on the GPU plus the inputs of every decode step."""
 
-    def __init__(self, name, seed=0, device="cuda", num_splits=0, gen_chunk=8, layers=None):
+    def __init__(self, name, seed=0, device="cuda", num_splits=0, gen_chunk=8, layers=None, fused=True):
         """layers: indices of the workload's layers to build (default all); a subset keeps every
-        layer's shapes, data and launches, and is used by the full-size parity tests."""
+        layer's shapes, data and launches, and is used by the full-size parity tests. fused: append
+        through the fused append-and-decode call (else quantize_append, then decode_attention)."""
+        self.fused = fused
         import torch
 
         import layer_wise_mixed_amd as kvq
@@ -143,12 +145,19 @@ class Workload:
         self.lens_after.add_(1)
 
     def step(self, i):
-        """Launch one decode step (all layers) for cycle position i."""
+        """Launch one decode step (all layers) for cycle position i: per layer, the token append
+        fused into the decode split pass (one launch, plus the merge with several splits), or
+        with fused=False the two calls."""
         kvq = self.kvq
         for l in range(self.L):
-            kvq.quantize_append(self.plan, l, self.cache, self.k_dec[l][i], self.v_dec[l][i], self.lens_before)
-            kvq.decode_attention(self.plan, l, self.cache, self.q[l][i], self.lens_after, self.max_len, self.scale,
-                                 self.out, None, self.ws, self.splits)
+            if self.fused:
+                kvq.append_decode_attention(self.plan, l, self.cache, self.k_dec[l][i], self.v_dec[l][i],
+                                            self.q[l][i], self.lens_before, self.max_len, self.scale, self.out,
+                                            None, self.ws, self.splits)
+            else:
+                kvq.quantize_append(self.plan, l, self.cache, self.k_dec[l][i], self.v_dec[l][i], self.lens_before)
+                kvq.decode_attention(self.plan, l, self.cache, self.q[l][i], self.lens_after, self.max_len,
+                                     self.scale, self.out, None, self.ws, self.splits)
         self.lens_before.add_(1)
         self.lens_after.add_(1)
 
@@ -403,6 +412,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--unfused", action="store_true",
+                    help="contiguous workloads: append with its own launch instead of inside the split pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
@@ -435,7 +446,9 @@ def main():
     kvq.load()
     t_setup = time.perf_counter()
     cls = PagedWorkload if WORKLOADS[args.workload].get("paged") else Workload
-    wl = cls(args.workload, seed=args.seed, num_splits=args.splits)
+    wl = cls(args.workload, seed=args.seed, num_splits=args.splits, **({} if cls is PagedWorkload else
+                                                                       {"fused": not args.unfused}))
+    fused = getattr(wl, "fused", False)
     K = args.steps if args.steps is not None else wl.C
     W = args.warmup if args.warmup is not None else min(wl.C, 16)
     print(f"# setup {time.perf_counter() - t_setup:.1f}s: {wl.w['desc']}, splits={wl.splits}", file=sys.stderr,
@@ -524,11 +537,13 @@ def main():
         "config": {"workload": args.workload, "description": wl.w["desc"], "layers": wl.L, "batch": wl.B,
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": 128, "context": [wl.P + 1, wl.P + wl.C],
                    "equiv_bits": wl.plan.equiv_bits, "splits": wl.splits,
-                   "launch": "eager" if graphs is None else "hip-graph per step",
+                   "launch": ("eager" if graphs is None else "hip-graph per step")
+                   + ("; token append fused into the split pass" if fused else "; append kernel, then split pass"),
                    "effective_GBps_whole_step": eff_gbs, "effective_frac_whole_step": eff_gbs / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": traffic,
-                     "kernel": "decode split pass", "avg_launch_us": avg_split_s * 1e6,
+                     "kernel": "decode split pass" + (" (with the fused token append)" if fused else ""),
+                     "avg_launch_us": avg_split_s * 1e6,
                      "timing": "HIP events bound to each split dispatch, eager pass over the same K steps",
                      "bytes_per_launch": bytes_launches / max(n_launch, 1)},
     }

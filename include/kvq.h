@@ -225,6 +225,35 @@ int kvq_decode_attention(const kvq_plan *plan, int32_t layer, const void *cache,
                          int32_t num_splits, const kvq_pages *pages, kvq_stream_t stream);
 
 /*
+ * kvq_append_decode_attention -- one decode step of one layer with its token
+ * append fused in: the same result, in the cache and in out/lse_out, as
+ * kvq_quantize_append with n_new = 1 followed by kvq_decode_attention with
+ * every seq_lens[r] one larger, in one split pass (plus the merge pass when
+ * there are several splits). The workgroup whose split holds the new
+ * token's place appends it: into the fp16 tail record, or, when it completes
+ * a 32-token group, by quantizing and packing that group before any wave
+ * reads it (TriAxialKV page, "Facts", quantizer bullet, as in
+ * kvq_quantize_append). This saves the append launch of every decode step.
+ *   k_new, v_new: device fp16 [batch][Hkv][1][128], the new token;
+ *   seq_lens: device [batch] tokens per request BEFORE the append (the
+ *     caller advances them afterwards, as with kvq_quantize_append); a
+ *     stream at max_tokens is left unchanged and attended as it is;
+ *   max_seq_len: host bound of seq_lens[r] + 1 (at least 1);
+ *   q, softmax_scale, out, out_dtype, lse_out, workspace, num_splits: as in
+ *     kvq_decode_attention (workspace sized by kvq_decode_workspace_bytes
+ *     with the same max_seq_len).
+ * Contiguous plans only: a paged pool uses the two calls.
+ *   Errors: INVALID_ARG, UNSUPPORTED (paged plan), CAPACITY (max_seq_len >
+ *   max_tokens), WORKSPACE, HIP.
+ */
+int kvq_append_decode_attention(const kvq_plan *plan, int32_t layer, void *cache,
+                                const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
+                                const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                float softmax_scale, void *out, int32_t out_dtype, float *lse_out,
+                                void *workspace, size_t workspace_bytes, int32_t num_splits,
+                                kvq_stream_t stream);
+
+/*
  * kvq_dequantize -- the cache of one layer back in fp32, for checking:
  * k_out, v_out: device fp32 [batch][Hkv][max_seq_len][128]; token j of
  * request r is fmaf(code, scale, zero) for quantized tokens and the stored

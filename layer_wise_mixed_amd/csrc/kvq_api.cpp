@@ -360,6 +360,69 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   return hip_status(e, "merge launch");
 }
 
+int kvq_append_decode_attention(const kvq_plan* plan, int32_t layer, void* cache, const uint16_t* k_new,
+                                const uint16_t* v_new, const uint16_t* q, const int32_t* seq_lens, int32_t batch,
+                                int32_t max_seq_len, float softmax_scale, void* out, int32_t out_dtype,
+                                float* lse_out, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                kvq_stream_t stream) {
+  int st = check_plan_layer(plan, layer);
+  if (st) return st;
+  if (is_paged(plan))
+    return fail(KVQ_ERR_UNSUPPORTED, "a paged pool appends and decodes with kvq_quantize_append and "
+                                     "kvq_decode_attention");
+  if (!cache || !k_new || !v_new || !q || !out) return fail(KVQ_ERR_INVALID_ARG, "null cache, input or output");
+  if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (batch < 0 || batch > plan->shape.max_batch)
+    return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
+  if (out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_F32)
+    return fail(KVQ_ERR_INVALID_ARG, "out_dtype %d", out_dtype);
+  if (num_splits < 0 || num_splits > 1024) return fail(KVQ_ERR_INVALID_ARG, "num_splits %d", num_splits);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (max_seq_len < 1) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 1 (it counts the appended token)", max_seq_len);
+  if (max_seq_len > capacity_tokens(plan, nullptr))
+    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > %lld tokens of capacity", max_seq_len,
+                (long long)capacity_tokens(plan, nullptr));
+  if (batch == 0) return ok();
+  const int32_t splits = num_splits ? num_splits : auto_splits(plan, batch, max_seq_len);
+  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
+  const int32_t gps = (nvg + splits - 1) / splits;
+  const size_t need = (size_t)batch * plan->shape.num_q_heads * splits * (kvq::D + 1) * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  kvq::DecodeArgs a;
+  a.geo = geom(plan, layer, cache);
+  a.pg = paged_geom(plan, layer, nullptr);
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.splits = splits;
+  a.groups_per_split = gps;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.part_o = (float*)workspace;
+  a.part_lse = a.part_o + (size_t)batch * plan->shape.num_q_heads * splits * kvq::D;
+  a.out = out;
+  a.out_f32 = out_dtype == KVQ_OUT_F32;
+  a.lse_out = lse_out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  hipStream_t s = (hipStream_t)stream;
+  kvq::EventPair ev;
+  bool timed = timer_slot(1, &ev);
+  hipError_t e = kvq::launch_decode_split_mfma(a, batch, s, timed ? &ev : nullptr);
+  if (e != hipSuccess) return hip_status(e, "fused append and split launch");
+  if (splits == 1) return ok();
+  kvq::MergeArgs m;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.splits = splits;
+  m.rows = batch * plan->shape.num_q_heads;
+  m.out = out;
+  m.out_f32 = out_dtype == KVQ_OUT_F32;
+  m.lse_out = lse_out;
+  timed = timer_slot(2, &ev);
+  e = kvq::launch_merge(m, s, timed ? &ev : nullptr);
+  return hip_status(e, "merge launch");
+}
+
 int kvq_dequantize(const kvq_plan* plan, int32_t layer, const void* cache, const int32_t* seq_lens, int32_t batch,
                    int32_t max_seq_len, float* k_out, float* v_out, const kvq_pages* pages, kvq_stream_t stream) {
   int st = check_plan_layer(plan, layer);

@@ -1,121 +1,16 @@
 // kvq_append.hip -- quantize-and-pack on append, and the checking dequantizer.
 //
-// Quantizer (TriAxialKV page, "Facts", quantizer bullet: asymmetric groupwise,
-// group size 32): scale = (max - min) / (2^b - 1) in fp32, zero = min,
-// code = clamp(rint((x - zero) / scale), 0, 2^b - 1) with IEEE division and
-// round-half-even; a constant group gets scale 0 and codes 0. Keys are grouped
-// per channel over 32 tokens (KVTuner summary page, "Facts": keys have
+// The group quantizer and packer are in kvq_quantize.h. Keys are grouped per
+// channel over 32 tokens (KVTuner summary page, "Facts": keys have
 // channel-wise outliers) or per token over 32 channels; values per token.
 // Tokens that do not fill a group stay fp16 in the stream's tail record.
 #include "kvq_internal.h"
+#include "kvq_quantize.h"
 
 #pragma clang fp contract(off)
 
 namespace kvq {
 namespace {
-
-__device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
-
-__device__ inline uint16_t tail_get(const uint8_t* rec, bool is_v, int j, int c) {
-  int lane, e;
-  if (is_v) v_site(j, c, &lane, &e); else k_site(j, c, &lane, &e);
-  const uint8_t* blk = rec + (is_v ? 8192 : 0);
-  return *(const uint16_t*)(blk + word_offset(lane, e >> 1) + (e & 1) * 2);
-}
-
-__device__ inline void tail_put(uint8_t* rec, bool is_v, int j, int c, uint16_t x) {
-  int lane, e;
-  if (is_v) v_site(j, c, &lane, &e); else k_site(j, c, &lane, &e);
-  uint8_t* blk = rec + (is_v ? 8192 : 0);
-  *(uint16_t*)(blk + word_offset(lane, e >> 1) + (e & 1) * 2) = x;
-}
-
-// One group of 32 values x[i * stride]; writes codes[i * cstride], returns scale/zero.
-__device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint16_t* codes,
-                                  int cstride, float* scale, float* zero) {
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll 8
-  for (int i = 0; i < GS; ++i) {
-    const float v = h2f(x[i * stride]);
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
-  }
-  const float levels = (float)((1 << bits) - 1);
-  const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
-  *scale = s;
-  *zero = mn;
-#pragma unroll 8
-  for (int i = 0; i < GS; ++i) {
-    uint16_t code = 0;
-    if (s != 0.0f) {
-      const float t = __fdiv_rn(__fsub_rn(h2f(x[i * stride]), mn), s);
-      float r = rintf(t);
-      r = fminf(fmaxf(r, 0.0f), levels);
-      code = (uint16_t)r;
-    }
-    codes[i * cstride] = code;
-  }
-}
-
-// Write the 512*bits bytes of a code block from codes[32][128] (token, channel).
-__device__ inline void pack_block(uint8_t* blk, const uint16_t (*codes)[D], int bits, bool is_v, int tid,
-                                  int nthreads) {
-  const int per_word = 32 / bits;
-  const int nwords = 128 * bits;
-  for (int W = tid; W < nwords; W += nthreads) {
-    const int lane = (W & 255) >> 2;
-    const int w = (W >> 8) * 4 + (W & 3);
-    uint32_t word = 0;
-    for (int p = 0; p < per_word; ++p) {
-      const int e = w * per_word + p;
-      int j, c;
-      if (is_v) v_inverse(lane, e, &j, &c); else k_inverse(lane, e, &j, &c);
-      const uint32_t code = codes[j][c];
-      word |= code << ((p & 1) * 16 + (p >> 1) * bits);
-    }
-    *(uint32_t*)(blk + (size_t)W * 4) = word;
-  }
-}
-
-// Quantize one full 32-token group (xs: fp16 K and V [32][128], in LDS) and
-// write its record; cs is LDS scratch for the codes. 256 threads.
-__device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][D], uint8_t* rec, int kb,
-                                       int vb, int k_token, int tid) {
-  const RecordParts parts = record_parts(kb, vb);
-  float* kmeta = (float*)(rec + parts.kmeta);
-  float* vmeta = (float*)(rec + parts.vmeta);
-  if (tid < 128) {
-    if (kb == 16) {
-      for (int i = 0; i < GS; ++i) cs[0][i][tid] = xs[0][i][tid];
-    } else if (!k_token) {
-      const int c = tid;
-      float s, z;
-      quantize32(&xs[0][0][c], D, kb, &cs[0][0][c], D, &s, &z);
-      kmeta[meta_channel(c)] = s;
-      kmeta[128 + meta_channel(c)] = z;
-    } else {
-      const int j = tid >> 2, n = tid & 3;
-      float s, z;
-      quantize32(&xs[0][j][32 * n], 1, kb, &cs[0][j][32 * n], 1, &s, &z);
-      kmeta[meta_token(j, n)] = s;
-      kmeta[128 + meta_token(j, n)] = z;
-    }
-  } else {
-    const int t2 = tid - 128;
-    if (vb == 16) {
-      for (int i = 0; i < GS; ++i) cs[1][i][t2] = xs[1][i][t2];
-    } else {
-      const int j = t2 >> 2, n = t2 & 3;
-      float s, z;
-      quantize32(&xs[1][j][32 * n], 1, vb, &cs[1][j][32 * n], 1, &s, &z);
-      vmeta[meta_token(j, n)] = s;
-      vmeta[128 + meta_token(j, n)] = z;
-    }
-  }
-  __syncthreads();
-  pack_block(rec, cs[0], kb, false, tid, blockDim.x);
-  pack_block(rec + parts.vcode, cs[1], vb, true, tid, blockDim.x);
-}
 
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ uint16_t xs[2][GS][D];

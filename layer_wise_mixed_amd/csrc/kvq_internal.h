@@ -184,6 +184,11 @@ struct DecodeArgs {
   void* out;             // with one split the split pass writes the final output ...
   int out_f32;
   float* lse_out;        // ... and log-sum-exp (nullable)
+  // Fused append of one token per request (contiguous streams): k_new/v_new
+  // fp16 [batch][hkv][128]; seq_lens then count the tokens before it. Null:
+  // a plain decode.
+  const uint16_t* k_new = nullptr;
+  const uint16_t* v_new = nullptr;
 };
 
 struct MergeArgs {

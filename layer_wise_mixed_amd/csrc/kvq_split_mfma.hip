@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "kvq_internal.h"
+#include "kvq_quantize.h"
 
 
 namespace kvq {
@@ -638,7 +639,94 @@ __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta,
   }
 }
 
-// Contiguous streams: one workgroup per (split, KV head, request).
+// Fused append, new token completes group m: the whole workgroup quantizes
+// the tail's 31 tokens and the new one into record m (the same quantizer and
+// packer as the append kernel), with xs/cs as LDS staging; the closing
+// barrier makes the record visible to the waves that load it.
+__device__ __forceinline__ void flush_group(uint8_t* stream, const LayerGeom& g, int m, const uint16_t* kn,
+                                            const uint16_t* vn, uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][D]) {
+  const int tid = threadIdx.x;
+  const uint8_t* tail = stream + g.tail_offset;
+  // the tail record as 1024 16-byte rows (lane l of 1 KiB row w: words 4w ..
+  // 4w + 3 of lane l), four a thread, all loads issued before any is used
+  u4_t rows[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) rows[q] = *(const u4_t*)(tail + (size_t)(tid + 256 * q) * 16);
+  const uint16_t nk = kn[tid & 127], nv = vn[tid & 127];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ch = tid + 256 * q;  // rows 0..511: keys, 512..1023: values
+    const bool is_v = ch >= 512;
+    const int lane = ch & 63, w0 = 4 * ((ch & 511) >> 6);
+#pragma unroll
+    for (int e2 = 0; e2 < 8; ++e2) {
+      const int e = 2 * w0 + e2;
+      int j, c;
+      if (is_v) v_inverse(lane, e, &j, &c); else k_inverse(lane, e, &j, &c);
+      if (j < GS - 1) xs[is_v][j][c] = (uint16_t)(rows[q][e2 >> 1] >> (16 * (e2 & 1)));
+    }
+  }
+  xs[tid >> 7][GS - 1][tid & 127] = tid < 128 ? nk : nv;  // the new token is slot 31
+  __syncthreads();
+  quantize_record(xs, cs, stream + (size_t)m * g.record_bytes, g.kb, g.vb, g.k_token, tid);
+  __syncthreads();
+}
+
+// Fused append, otherwise: the new token into tail slot j, for the wave
+// that owns the tail, once it has loaded the tail record into kw/vw (the
+// K16V16 layout). Each lane loads its own pieces of the token (keys: lanes
+// j%16 + 16a hold channels 32s + 8a .. + 7 at words 16(j/16) + 4s .. + 3;
+// values: lanes 16((j%16)/4) + c%16 hold channel c%16 + 16u at word
+// 4u + 2(j/16) + (j%4)/2, half j%2), puts them into its registers, and
+// stores them into the tail record for later steps (the bytes the append
+// kernel writes).
+__device__ __forceinline__ void merge_new_token(uint8_t* tail, const uint16_t* kn, const uint16_t* vn, int j, int lane,
+                                                uint32_t* kw, uint32_t* vw) {
+  const bool kl = (lane & 15) == (j & 15);
+  const bool vl = (lane >> 4) == ((j & 15) >> 2);
+  const int a4 = lane >> 4, cl = lane & 15;
+  u4_t kv[4];
+  uint16_t vv[8];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) kv[s4] = kl ? *(const u4_t*)(kn + 32 * s4 + 8 * a4) : u4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) vv[u] = vl ? vn[16 * u + cl] : (uint16_t)0;
+  if (kl) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) *(u4_t*)(tail + word_offset(lane, 16 * (j >> 4) + 4 * s4)) = kv[s4];
+  }
+  if (vl) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = 8 * u + 4 * (j >> 4) + (j & 3);
+      *(uint16_t*)(tail + 8192 + word_offset(lane, e >> 1) + (e & 1) * 2) = vv[u];
+    }
+  }
+  // every register index static: each word takes the new piece or keeps its
+  // value by a select (an index computed from j would put kw/vw in scratch)
+  const bool hi16 = j >= 16;
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kw[4 * s4 + i] = kl && !hi16 ? kv[s4][i] : kw[4 * s4 + i];
+      kw[16 + 4 * s4 + i] = kl && hi16 ? kv[s4][i] : kw[16 + 4 * s4 + i];
+    }
+  const int wsel = 2 * (j >> 4) + ((j & 3) >> 1);
+  const int hs = 16 * (j & 1);
+  const uint32_t keep = ~(0xFFFFu << hs);
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      vw[4 * u + w] = vl && w == wsel ? (vw[4 * u + w] & keep) | ((uint32_t)vv[u] << hs) : vw[4 * u + w];
+}
+
+// Contiguous streams: one workgroup per (split, KV head, request). With
+// a.k_new set, the pass also appends one token per request (as the append
+// kernel would with n_new = 1) and attends over the cache including it: a
+// token that completes a group is packed before the loop starts; one that
+// goes to the tail joins the tail pass at the end.
 template <int KB, int VB, bool KTOK, int NS>
 __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   constexpr int R = (KB < 16 && !KTOK) ? NS : 1;
@@ -646,7 +734,11 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   const LayerGeom& g = a.geo;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-  int L = a.seq_lens[r];
+  const int L0 = a.seq_lens[r];
+  // a fused append adds token L0 where the append kernel would (0 <= L0 <
+  // capacity); the attention covers the lengths a decode after it would see
+  const bool app = a.k_new != nullptr && L0 >= 0 && L0 < g.max_tokens;
+  int L = a.k_new != nullptr && L0 < g.max_tokens ? L0 + 1 : L0;
   if (L < 0) L = 0;
   if (L > g.max_tokens) L = g.max_tokens;
   const int nq = L / GS;
@@ -654,7 +746,20 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   const int nvg = nq + (T > 0);
   const int g0 = split * a.groups_per_split;
   const int g1 = min(g0 + a.groups_per_split, nvg);
-  const uint8_t* stream = g.base + (size_t)(r * g.hkv + h) * g.stream_bytes;
+  uint8_t* stream = g.base + (size_t)(r * g.hkv + h) * g.stream_bytes;
+  const size_t sigma = (size_t)r * g.hkv + h;
+  const uint16_t* kn = app ? a.k_new + sigma * D : nullptr;
+  const uint16_t* vn = app ? a.v_new + sigma * D : nullptr;
+  if (app) {
+    if (L0 % GS == GS - 1) {
+      const int m = L0 / GS;
+      if (m >= g0 && m < g1) {
+        static_assert(sizeof(sm.o) >= 4 * GS * D * sizeof(uint16_t), "the staging fits the result buffer");
+        uint16_t(*xs)[GS][D] = reinterpret_cast<uint16_t(*)[GS][D]>(&sm.o[0][0][0]);
+        flush_group(stream, g, m, kn, vn, xs, xs + 2);
+      }
+    }
+  }
 
   Lane ln;
   Acc acc;
@@ -675,10 +780,11 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   // the fp16 tail last (its registers are free now), by the wave that owns
   // it, in true units: the accumulators go to true units and back
   if (T > 0 && nq >= g0 && nq < g1 && ((nq - g0) & (kWaves - 1)) == wave) {
-    const uint8_t* rec = stream + g.tail_offset;
+    uint8_t* rec = stream + g.tail_offset;
     uint32_t kw[32], vw[32];
     load_codes<16>(rec, ln.lane, kw);
     load_codes<16>(rec + 8192, ln.lane, vw);
+    if (app) merge_new_token(rec, kn, vn, T - 1, ln.lane, kw, vw);  // T > 0: the token went to the tail
     if constexpr (VB < 16) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {

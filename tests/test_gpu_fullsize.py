@@ -1,9 +1,12 @@
 """Parity at full size. The benchmark's workloads are built exactly as the benchmark builds them
 (a subset of their layers: each built layer has the benchmark's shapes, data, split count and
-launches), stepped through their decode cycle with the benchmark's own step (append + decode),
+launches), stepped through their decode cycle with the benchmark's own step (the token append
+fused into the decode split pass for contiguous caches; append, then decode for the paged pool),
 and checked on sampled (request, KV head) streams: packed bytes bit-exact against the oracle's
 packing of the regenerated stream, attention within the stated tolerance of the oracle's fp64
-attention. Every other request of the batch is computed in the same launches."""
+attention. Every other request of the batch is computed in the same launches. The fused step's
+own output (fp16, last built layer) must equal bit for bit a separate decode over the cache it
+left."""
 import math
 import os
 import sys
@@ -82,6 +85,13 @@ def test_fullsize_contiguous(gpu, oq, name, layers, positions):
             continue
         torch.cuda.synchronize()
         L = wl.P + pos + 1
+        if wl.fused:
+            last = wl.L - 1
+            out16 = torch.full_like(wl.out, float("nan"))
+            wl.kvq.decode_attention(wl.plan, last, wl.cache, wl.q[last][pos], wl.lens_before, wl.max_len, wl.scale,
+                                    out16, None, wl.ws, wl.splits)
+            torch.cuda.synchronize()
+            assert torch.equal(out16, wl.out), f"{name} L{L}: fused step output differs from a decode after it"
         for l, li in enumerate(wl.layer_ids):
             lp = wl.plan.layers[l]
             kb, vb, kt = lp.k_bits, lp.v_bits, lp.k_axis == 1

@@ -156,6 +156,28 @@ def test_append_and_dequant_argument_errors(lib):
     assert lib.kvq_dequantize(None, 0, f, f, 2, 30, f, f, None, None) == kvq.ERR_INVALID_ARG
 
 
+def test_fused_append_decode_argument_errors(lib):
+    plan = kvq.plan_layers(kvq.make_shape(32, 8, 4, max_tokens=256), [(8, 4)] * 2)
+    f = ctypes.c_void_p(0x1000)
+
+    def call(plan=plan, layer=0, batch=2, max_seq_len=64, ws_bytes=1 << 30, splits=0, seq=True, kn=True):
+        return lib.kvq_append_decode_attention(ctypes.byref(plan), layer, f, f if kn else None, f, f,
+                                               f if seq else None, batch, max_seq_len, ctypes.c_float(0.088), f, 0,
+                                               None, f, ws_bytes, splits, None)
+
+    assert call(layer=2) == kvq.ERR_INVALID_ARG
+    assert call(batch=5) == kvq.ERR_INVALID_ARG
+    assert call(max_seq_len=257) == kvq.ERR_CAPACITY
+    assert call(max_seq_len=0) == kvq.ERR_INVALID_ARG  # it counts the appended token
+    assert call(ws_bytes=16) == kvq.ERR_WORKSPACE
+    assert call(splits=2000) == kvq.ERR_INVALID_ARG
+    assert call(seq=False) == kvq.ERR_INVALID_ARG
+    assert call(kn=False) == kvq.ERR_INVALID_ARG
+    assert call(plan=_paged_plan()) == kvq.ERR_UNSUPPORTED
+    assert "paged" in lib.kvq_last_error().decode()
+    assert call(batch=0) == kvq.OK  # nothing to do
+
+
 def test_auto_split_count():
     plan = kvq.plan_layers(kvq.make_shape(32, 8, 64, max_tokens=2080), [(4, 2)])
     s = kvq.num_splits(plan, 0, 64, 2048)
