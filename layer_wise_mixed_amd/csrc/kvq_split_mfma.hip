@@ -685,12 +685,15 @@ __device__ __forceinline__ void merge_new_token(uint8_t* tail, const uint16_t* k
   const bool kl = (lane & 15) == (j & 15);
   const bool vl = (lane >> 4) == ((j & 15) >> 2);
   const int a4 = lane >> 4, cl = lane & 15;
+  // every lane loads (valid addresses for all): a load under a lane condition
+  // would make the compiler wait for all loads in flight (the tail's too)
+  // before the other lanes' values could be written to the same registers
   u4_t kv[4];
   uint16_t vv[8];
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) kv[s4] = kl ? *(const u4_t*)(kn + 32 * s4 + 8 * a4) : u4_t{0, 0, 0, 0};
+  for (int s4 = 0; s4 < 4; ++s4) kv[s4] = *(const u4_t*)(kn + 32 * s4 + 8 * a4);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) vv[u] = vl ? vn[16 * u + cl] : (uint16_t)0;
+  for (int u = 0; u < 8; ++u) vv[u] = vn[16 * u + cl];
   if (kl) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) *(u4_t*)(tail + word_offset(lane, 16 * (j >> 4) + 4 * s4)) = kv[s4];
