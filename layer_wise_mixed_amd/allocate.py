@@ -86,3 +86,21 @@ def allocate(counts, d2, d4, budget: float):
     if len(n) <= EXHAUSTIVE_MAX_TAGS:
         return _exhaustive(n, a, b, budget)
     return _greedy(n, a, b, budget)
+
+
+def int2_tokens(tags, bits_per_tag):
+    """Which tokens of one request the paged pool stores as INT2, given each
+    token's tag (arrival order) and the allocation: the tokens of INT2 tags,
+    taken in arrival order in runs of 32 (a key group spans 32 tokens); the
+    last len % 32 of them go through the INT4 per-token path with every
+    other token (TriAxialKV page, "Facts": leftover INT2 tokens take the INT4
+    path). Returns (int2 token indices, a multiple of 32 long; INT4 token
+    indices), both in arrival order."""
+    tags = np.asarray(tags)
+    is2 = np.asarray(bits_per_tag)[tags] == 2
+    cand = np.flatnonzero(is2)
+    n2 = len(cand) - len(cand) % 32
+    int2 = cand[:n2]
+    rest = np.ones(len(tags), dtype=bool)
+    rest[int2] = False
+    return int2.tolist(), np.flatnonzero(rest).tolist()

@@ -86,3 +86,15 @@ def test_library_exhaustive_at_22_tags():
         alt[k] = 6 - alt[k]
         if sum(n * b for n, b in zip(counts, alt)) <= 3.0 * sum(counts):
             assert total(alt) >= total(bits)
+
+
+def test_int2_tokens_whole_runs_and_leftovers():
+    tags = [0] * 40 + [1] * 10 + [0] * 30 + [2] * 5
+    int2, int4 = lib_alloc.int2_tokens(tags, [2, 4, 2])
+    # tag 0 and 2 tokens in arrival order: 0..39, 50..79, 80..84 -> 75 of them, 64 in two runs
+    cand = list(range(40)) + list(range(50, 85))
+    assert int2 == cand[:64]
+    assert int4 == sorted(set(range(85)) - set(cand[:64]))
+    assert len(int2) % 32 == 0
+    int2, int4 = lib_alloc.int2_tokens([1] * 20, [2, 4])
+    assert int2 == [] and int4 == list(range(20))
