@@ -18,10 +18,17 @@ applied with no online decision). Here, with no model or dataset:
   choose()    -- one surviving pair per layer with the least total error
                  whose mean (bK + bV) / 2 is within a bit budget (an exact
                  dynamic program over the integer total of bK + bV).
-  search()    -- the three in a row; returns the map and its figures.
+  frontier()  -- the least total error at every total bit count where it
+                 drops: the maps of every budget from one table (the search's
+                 two objectives, bits and error).
+  cluster_layers(), choose_clustered() -- inter-layer clustering: layers with
+                 close error profiles share one pair, which shrinks the
+                 search to one choice per cluster.
+  search()    -- profile, prune and choose (optionally by clusters); returns
+                 the map, its figures and the frontier.
 
 Run as ``python -m layer_wise_mixed_amd.search --hq 32 --hkv 8 --layers 32
---budget 3.25`` to print a map as JSON.
+--budget 3.25`` to print a map as JSON (``--tau T`` clusters first).
 """
 from __future__ import annotations
 
@@ -92,12 +99,10 @@ def prune(bits, errs) -> list[int]:
     return sorted(keep)
 
 
-def choose(options, budget_total: int):
-    """options[l]: list of (bits, err), bits = bK + bV. Returns (choices, total
-    error) with sum of bits <= budget_total and the least total error (ties:
-    fewer bits, then earlier options), or None if nothing fits."""
+def _table(options, B: int):
+    """cost[b]: the least error of all layers spending exactly b bits (inf if
+    none), with per-layer back pointers."""
     n = len(options)
-    B = budget_total
     inf = math.inf
     # cost[b]: least error of layers 0..l-1 spending exactly b bits
     cost = np.full(B + 1, inf)
@@ -116,35 +121,112 @@ def choose(options, budget_total: int):
             pick[better] = i
         cost = new
         back.append(pick)
-    if not np.isfinite(cost).any():
-        return None
-    b = int(np.argmin(cost))  # the least error; np.argmin takes the fewest bits among equal ones
-    total = float(cost[b])
-    choices = [0] * n
-    for l in range(n - 1, -1, -1):
+    return cost, back
+
+
+def _walk_back(options, back, b: int):
+    choices = [0] * len(options)
+    for l in range(len(options) - 1, -1, -1):
         i = int(back[l][b])
         choices[l] = i
         b -= options[l][i][0]
-    return choices, total
+    return choices
 
 
-def search(hq: int, hkv: int, num_layers: int, budget: float, pairs=PAIRS, **profile_kw):
-    """Profile every layer, prune each layer's pairs, and choose the map.
+def choose(options, budget_total: int):
+    """options[l]: list of (bits, err), bits = bK + bV. Returns (choices, total
+    error) with sum of bits <= budget_total and the least total error (ties:
+    fewer bits, then earlier options), or None if nothing fits."""
+    cost, back = _table(options, budget_total)
+    if not np.isfinite(cost).any():
+        return None
+    b = int(np.argmin(cost))  # the least error; np.argmin takes the fewest bits among equal ones
+    return _walk_back(options, back, b), float(cost[b])
+
+
+def frontier(options):
+    """Maps for every budget at once (the two objectives of the search: total
+    bits and total error): [(total bits, least total error, choices)] at every
+    total bit count where the least error drops below that of all smaller
+    counts, ascending. One table serves every budget."""
+    B = sum(max(b for b, _ in o) for o in options)
+    cost, back = _table(options, B)
+    out = []
+    best = math.inf
+    for b in range(B + 1):
+        if cost[b] < best:
+            best = float(cost[b])
+            out.append((b, best, _walk_back(options, back, b)))
+    return out
+
+
+def cluster_layers(errors, tau: float):
+    """Inter-layer clustering (KVTuner summary page, "Method"): layers whose
+    error profiles over the pairs are close share one pair. Distance of two
+    layers: the largest difference of their log errors; clusters: complete
+    linkage, merged while the closest two are at most tau apart. Returns
+    sorted lists of layer indices, ordered by their first layer."""
+    from scipy.cluster.hierarchy import fcluster, linkage
+
+    e = np.log(np.maximum(np.asarray(errors, dtype=np.float64), 1e-300))
+    if len(e) == 1:
+        return [[0]]
+    labels = fcluster(linkage(e, method="complete", metric="chebyshev"), t=tau, criterion="distance")
+    groups = {}
+    for l, lab in enumerate(labels):
+        groups.setdefault(int(lab), []).append(l)
+    return sorted(groups.values(), key=lambda c: c[0])
+
+
+def choose_clustered(errors, bits, clusters, budget_total: int):
+    """One pair per cluster, every layer of a cluster taking it: the least
+    total error within budget_total bits (the clusters' pairs pruned first).
+    Returns (pair index per layer, total error) or None."""
+    errors = np.asarray(errors, dtype=np.float64)
+    kept, options = [], []
+    for c in clusters:
+        cb = [len(c) * b for b in bits]
+        ce = [float(errors[c, p].sum()) for p in range(len(bits))]
+        k = prune(cb, ce)
+        kept.append(k)
+        options.append([(cb[p], ce[p]) for p in k])
+    res = choose(options, budget_total)
+    if res is None:
+        return None
+    per_layer = [0] * len(errors)
+    for c, k, i in zip(clusters, kept, res[0]):
+        for l in c:
+            per_layer[l] = k[i]
+    return per_layer, res[1]
+
+
+def search(hq: int, hkv: int, num_layers: int, budget: float, pairs=PAIRS, tau=None, **profile_kw):
+    """Profile every layer, prune each layer's pairs, and choose the map
+    (with tau: one pair per cluster of layers within tau of each other).
     Returns a dict: map (one (bK, bV) per layer), equiv_bits, total_error,
-    the per-layer kept pair indices and the error table."""
+    the per-layer kept pair indices, the clusters, the error table and the
+    per-layer frontier [(equiv bits, total error)]."""
     layers = list(range(num_layers))
     errs = profile(hq, hkv, layers, pairs, **profile_kw)
     bits = [kb + vb for kb, vb in pairs]
     kept = [prune(bits, list(errs[i])) for i in range(num_layers)]
     options = [[(bits[j], float(errs[i, j])) for j in kept[i]] for i in range(num_layers)]
     budget_total = int(math.floor(2 * num_layers * budget + 1e-9))
-    res = choose(options, budget_total)
+    clusters = None
+    if tau is None:
+        res = choose(options, budget_total)
+        if res is not None:
+            res = ([kept[i][c] for i, c in enumerate(res[0])], res[1])
+    else:
+        clusters = cluster_layers(errs, tau)
+        res = choose_clustered(errs, bits, clusters, budget_total)
     if res is None:
         raise ValueError(f"budget {budget} bits is below every map of these pairs")
-    choices, total = res
-    chosen = [pairs[kept[i][c]] for i, c in enumerate(choices)]
+    chosen = [pairs[p] for p in res[0]]
+    front = [(b / (2 * num_layers), e) for b, e, _ in frontier(options)]
     return {"map": [list(p) for p in chosen], "equiv_bits": sum(kb + vb for kb, vb in chosen) / (2 * num_layers),
-            "total_error": total, "kept": kept, "errors": errs.tolist(), "pairs": [list(p) for p in pairs]}
+            "total_error": res[1], "kept": kept, "clusters": clusters, "errors": errs.tolist(),
+            "pairs": [list(p) for p in pairs], "frontier": front}
 
 
 def main(argv=None):
@@ -158,9 +240,10 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--outliers", type=float, nargs=2, default=(4, 10.0), metavar=("COUNT", "FACTOR"))
     ap.add_argument("--per-token-keys", action="store_true")
+    ap.add_argument("--tau", type=float, default=None, help="cluster layers within this log-error distance")
     args = ap.parse_args(argv)
     t0 = time.perf_counter()
-    res = search(args.hq, args.hkv, args.layers, args.budget, batch=args.batch, seq_len=args.seq_len,
+    res = search(args.hq, args.hkv, args.layers, args.budget, tau=args.tau, batch=args.batch, seq_len=args.seq_len,
                  seed=args.seed, outliers=(int(args.outliers[0]), args.outliers[1]),
                  k_axis=1 if args.per_token_keys else 0)
     res["seconds"] = time.perf_counter() - t0

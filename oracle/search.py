@@ -25,6 +25,10 @@ Functions:
                   definition of dominance
   best_map     -- one option per layer, minimum total error under a total
                   bit budget, by the plain recursion over layers and budget
+  frontier     -- the least total error at every total bit count where it
+                  drops (best_map at every budget)
+  cluster_layers, best_clustered_map -- inter-layer clustering by complete
+                  linkage on log errors, and one pair per cluster
 """
 from __future__ import annotations
 
@@ -100,3 +104,75 @@ def best_map(options, budget: int):
     if res is None:
         return None
     return list(res[2]), res[0]
+
+
+# ---------------------------------------------------------------------------
+# Maps for every budget, and inter-layer clustering (KVTuner summary page,
+# "Method": a multi-objective search over per-layer pairs, with inter-layer
+# clustering shrinking its space). Readings: the two objectives are the total
+# bits and the total error, and the frontier is every total bit count whose
+# least error is below that of every smaller count; two layers' distance is
+# the largest difference of their log errors over the pairs; clusters are
+# formed by complete-linkage agglomeration while the closest two clusters are
+# at most tau apart (the distance of two clusters: the largest distance
+# between their members); a cluster takes one pair for all its layers.
+
+def frontier(options):
+    """[(total bits, least total error, choice)] for every total bit count
+    at which the least error (at most that many bits) drops, ascending."""
+    lo = sum(min(b for b, _ in o) for o in options)
+    hi = sum(max(b for b, _ in o) for o in options)
+    out = []
+    for b in range(lo, hi + 1):
+        res = best_map(options, b)
+        if res is None:
+            continue
+        bits = sum(options[l][c][0] for l, c in enumerate(res[0]))
+        if bits != b:
+            continue  # the least error at this budget was already reached with fewer bits
+        if not out or res[1] < out[-1][1]:
+            out.append((b, res[1], res[0]))
+    return out
+
+
+def layer_distance(e1, e2) -> float:
+    return max(abs(math.log(max(a, 1e-300)) - math.log(max(b, 1e-300))) for a, b in zip(e1, e2))
+
+
+def cluster_layers(errors, tau: float):
+    """errors[l][p]: layer l's error under pair p. Returns clusters as sorted
+    lists of layer indices, ordered by their first layer."""
+    clusters = [[l] for l in range(len(errors))]
+
+    def diameter(c):
+        return max((layer_distance(errors[i], errors[j]) for i in c for j in c), default=0.0)
+
+    while len(clusters) > 1:
+        best = None
+        for a in range(len(clusters)):
+            for b in range(a + 1, len(clusters)):
+                d = diameter(clusters[a] + clusters[b])
+                if best is None or d < best[0]:
+                    best = (d, a, b)
+        if best[0] > tau:
+            break
+        _, a, b = best
+        merged = sorted(clusters[a] + clusters[b])
+        clusters = [c for k, c in enumerate(clusters) if k not in (a, b)] + [merged]
+        clusters.sort(key=lambda c: c[0])
+    return clusters
+
+
+def best_clustered_map(errors, bits, clusters, budget: int):
+    """One pair per cluster (every layer of a cluster takes it): the least
+    total error with at most `budget` total bits. Returns (pair index per
+    layer, total error) or None."""
+    options = [[(len(c) * bits[p], sum(errors[l][p] for l in c)) for p in range(len(bits))] for c in clusters]
+    res = best_map(options, budget)
+    if res is None:
+        return None
+    per_layer = [0] * len(errors)
+    for c, p in zip(clusters, res[0]):
+        for l in c:
+            per_layer[l] = p
+    return per_layer, res[1]

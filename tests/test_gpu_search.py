@@ -71,3 +71,33 @@ def test_map_matches_oracle_choice(profiled, oracle_errs, budget):
     assert sum(kb + vb for kb, vb in got_pairs) <= total_budget
     assert got_pairs == want_pairs
     assert got[1] == pytest.approx(want[1], rel=1e-3)
+
+
+def test_frontier_matches_oracle(profiled, oracle_errs):
+    search, errs = profiled
+    bits = [kb + vb for kb, vb in search.PAIRS]
+    o_opts, l_opts = [], []
+    for i in range(len(LAYERS)):
+        ko = osearch.pareto_front([(bits[j], float(oracle_errs[i, j])) for j in range(len(bits))])
+        o_opts.append([(bits[j], float(oracle_errs[i, j])) for j in ko])
+        kl = search.prune(bits, list(errs[i]))
+        l_opts.append([(bits[j], float(errs[i, j])) for j in kl])
+    want = osearch.frontier(o_opts)
+    got = search.frontier(l_opts)
+    assert [b for b, _, _ in got] == [b for b, _, _ in want]
+    for (_, eg, _), (_, ew, _) in zip(got, want):
+        assert eg == pytest.approx(ew, rel=1e-3)
+
+
+@pytest.mark.parametrize("tau", [0.05, 0.3, 1.0])
+def test_clustered_map_matches_oracle(profiled, oracle_errs, tau):
+    search, errs = profiled
+    bits = [kb + vb for kb, vb in search.PAIRS]
+    want_cl = osearch.cluster_layers(oracle_errs, tau)
+    got_cl = search.cluster_layers(errs, tau)
+    assert got_cl == want_cl
+    budget = int(math.floor(2 * len(LAYERS) * 3.5 + 1e-9))
+    want = osearch.best_clustered_map(oracle_errs, bits, want_cl, budget)
+    got = search.choose_clustered(errs, bits, got_cl, budget)
+    assert got[0] == want[0]
+    assert got[1] == pytest.approx(want[1], rel=1e-3)

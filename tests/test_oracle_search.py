@@ -157,3 +157,110 @@ def test_library_choose_equals_oracle(seed):
     bits = lambda ch: sum(options[l][c][0] for l, c in enumerate(ch))
     assert bits(got[0]) == bits(want[0]) <= budget
     assert sum(options[l][c][1] for l, c in enumerate(got[0])) == got[1]
+
+
+# ------------------------------------------------ frontier and inter-layer clustering
+
+
+def _brute_frontier(options):
+    pts = {}
+    for choice in itertools.product(*[range(len(o)) for o in options]):
+        b = sum(options[l][c][0] for l, c in enumerate(choice))
+        e = sum(options[l][c][1] for l, c in enumerate(choice))
+        pts[b] = min(pts.get(b, math.inf), e)
+    out, best = [], math.inf
+    for b in sorted(pts):
+        if pts[b] < best:
+            best = pts[b]
+            out.append((b, best))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(15))
+def test_frontier_matches_brute_force(seed):
+    rng = np.random.default_rng(3000 + seed)
+    L = int(rng.integers(1, 5))
+    options = [[(int(rng.choice([4, 6, 8, 10, 12, 16])), int(rng.integers(0, 64)) / 1024)
+                for _ in range(int(rng.integers(1, 5)))] for _ in range(L)]
+    want = _brute_frontier(options)
+    got = osearch.frontier(options)
+    assert [(b, e) for b, e, _ in got] == want
+    for b, e, ch in got:
+        assert sum(options[l][c][0] for l, c in enumerate(ch)) == b
+        assert sum(options[l][c][1] for l, c in enumerate(ch)) == e
+    lib = lib_search.frontier(options)
+    assert [(b, e) for b, e, _ in lib] == want
+
+
+def _profiles(rng, L, P=9):
+    return np.exp(rng.normal(-3.0, 1.0, (L, P)))
+
+
+def test_clustering_hand_cases():
+    base = np.array([0.01, 0.02, 0.05, 0.1])
+    errs = np.stack([base, base, base * 1.05, base * 3.0, base * 3.1])
+    # log distances: layers 0, 1 identical; 2 is log(1.05) = 0.049 away; 3, 4 are log(3.1/3) = 0.033 apart
+    assert osearch.cluster_layers(errs, 0.0) == [[0, 1], [2], [3], [4]]
+    assert osearch.cluster_layers(errs, 0.04) == [[0, 1], [2], [3, 4]]
+    assert osearch.cluster_layers(errs, 0.1) == [[0, 1, 2], [3, 4]]
+    assert osearch.cluster_layers(errs, 10.0) == [[0, 1, 2, 3, 4]]
+    for tau in (0.0, 0.04, 0.1, 10.0):
+        assert lib_search.cluster_layers(errs, tau) == osearch.cluster_layers(errs, tau)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_clusters_are_tight_and_separated(seed):
+    rng = np.random.default_rng(4000 + seed)
+    errs = _profiles(rng, int(rng.integers(2, 9)))
+    tau = float(rng.uniform(0.5, 3.0))
+    cl = osearch.cluster_layers(errs, tau)
+    assert sorted(l for c in cl for l in c) == list(range(len(errs)))
+    diam = lambda c: max((osearch.layer_distance(errs[i], errs[j]) for i in c for j in c), default=0.0)
+    for c in cl:
+        assert diam(c) <= tau
+    for a in range(len(cl)):
+        for b in range(a + 1, len(cl)):
+            assert diam(cl[a] + cl[b]) > tau  # the agglomeration stopped: no two clusters fit together
+    assert lib_search.cluster_layers(errs, tau) == cl
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_clustered_map_matches_brute_force(seed):
+    rng = np.random.default_rng(5000 + seed)
+    L = int(rng.integers(2, 6))
+    errs = np.round(_profiles(rng, L, 4) * 1024) / 1024 + 1 / 1024
+    bits = [4, 6, 8, 12]
+    clusters = osearch.cluster_layers(errs, float(rng.uniform(0.2, 2.0)))
+    budget = int(rng.integers(4 * L, 12 * L + 1))
+    best = None
+    for choice in itertools.product(range(len(bits)), repeat=len(clusters)):
+        per = [0] * L
+        for c, p in zip(clusters, choice):
+            for l in c:
+                per[l] = p
+        b = sum(bits[p] for p in per)
+        if b > budget:
+            continue
+        e = sum(errs[l][p] for l, p in enumerate(per))
+        if best is None or (e, b) < best[:2]:
+            best = (e, b, per)
+    got = osearch.best_clustered_map(errs, bits, clusters, budget)
+    lib = lib_search.choose_clustered(errs, bits, clusters, budget)
+    if best is None:
+        assert got is None and lib is None
+        return
+    for res in (got, lib):
+        per, e = res
+        assert e == best[0] and sum(bits[p] for p in per) == best[1]
+        for c in clusters:
+            assert len({per[l] for l in c}) == 1  # one pair per cluster
+
+
+def test_singleton_clusters_equal_the_per_layer_choice():
+    rng = np.random.default_rng(6)
+    errs = np.round(_profiles(rng, 5, 4) * 1024) / 1024 + 1 / 1024
+    bits = [4, 6, 8, 12]
+    options = [[(bits[p], errs[l][p]) for p in range(4)] for l in range(5)]
+    want = osearch.best_map(options, 35)
+    got = osearch.best_clustered_map(errs, bits, [[l] for l in range(5)], 35)
+    assert got[1] == want[1] and got[0] == want[0]
