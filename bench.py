@@ -139,6 +139,33 @@ class Workload:
         return syn.keys_fp16(self.seed, layer, requests, range(self.Hkv), t0, n, outlier_count=cnt,
                              outlier_factor=fac, num_kv_heads=self.Hkv, device=device)
 
+    def prefill_append_rate(self, reps=3):
+        """The first layer's prefill for the whole batch in one append call (every full group
+        quantized and packed, the rest to the tail), timed with events around `reps` calls. It
+        rewrites the same bytes the prefill wrote. Bytes: the fp16 K and V read, the records and
+        tail slots written."""
+        import torch
+
+        kvq = self.kvq
+        li = self.layer_ids[0]
+        k = self.keys(li, range(self.B), 0, self.P, "cuda")
+        v = syn.values_fp16(self.seed, li, range(self.B), range(self.Hkv), 0, self.P, device="cuda")
+        zeros = torch.zeros(self.B, dtype=torch.int32, device="cuda")
+        kvq.quantize_append(self.plan, 0, self.cache, k, v, zeros)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            kvq.quantize_append(self.plan, 0, self.cache, k, v, zeros)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps / 1e3
+        lp = self.plan.layers[0]
+        streams = self.B * self.Hkv
+        nbytes = streams * self.P * 128 * 2 * 2 + streams * ((self.P // 32) * lp.record_bytes + (self.P % 32) * 512)
+        return {"layer": li, "format": f"K{lp.k_bits}V{lp.v_bits}", "tokens": self.B * self.P, "us": t * 1e6,
+                "bytes": nbytes, "GBps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / HBM_PEAK_GBS}
+
     def reset(self):
         self.lens_before.copy_(self.lens_base)
         self.lens_after.copy_(self.lens_base)
@@ -547,6 +574,12 @@ def main():
                      "timing": "HIP events bound to each split dispatch, eager pass over the same K steps",
                      "bytes_per_launch": bytes_launches / max(n_launch, 1)},
     }
+    if hasattr(wl, "prefill_append_rate"):
+        # the quantize-and-pack kernel at prefill size (HBM-bound there), reported beside the step
+        result["prefill_append"] = wl.prefill_append_rate()
+        print(f"# prefill append, layer {result['prefill_append']['layer']}: "
+              f"{result['prefill_append']['us']:.1f} us, {result['prefill_append']['GBps']:.0f} GB/s", file=sys.stderr,
+              flush=True)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)

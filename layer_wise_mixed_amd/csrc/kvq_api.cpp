@@ -71,6 +71,9 @@ bool timer_slot(int kind, kvq::EventPair* ev) {
 
 // ----------------------------------------------------------- arguments
 
+// The kernels read the cache, the new tokens and q in 16-byte pieces.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 int check_plan_layer(const kvq_plan* plan, int32_t layer) {
   if (!plan) return fail(KVQ_ERR_INVALID_ARG, "plan is NULL");
   if (plan->num_layers < 1 || plan->num_layers > KVQ_MAX_LAYERS)
@@ -256,6 +259,8 @@ int kvq_quantize_append(const kvq_plan* plan, int32_t layer, void* cache, const 
   int st = check_plan_layer(plan, layer);
   if (st) return st;
   if (!cache || !k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "null cache or input pointer");
+  if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(KVQ_ERR_INVALID_ARG, "cache, k_new and v_new must be 16-byte aligned");
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
   if (n_new < 0) return fail(KVQ_ERR_INVALID_ARG, "n_new %d < 0", n_new);
@@ -299,6 +304,7 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   int st = check_plan_layer(plan, layer);
   if (st) return st;
   if (!cache || !q || !out) return fail(KVQ_ERR_INVALID_ARG, "null cache, q or out");
+  if (!aligned16(cache) || !aligned16(q)) return fail(KVQ_ERR_INVALID_ARG, "cache and q must be 16-byte aligned");
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
   if (out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_F32)
@@ -371,6 +377,8 @@ int kvq_append_decode_attention(const kvq_plan* plan, int32_t layer, void* cache
     return fail(KVQ_ERR_UNSUPPORTED, "a paged pool appends and decodes with kvq_quantize_append and "
                                      "kvq_decode_attention");
   if (!cache || !k_new || !v_new || !q || !out) return fail(KVQ_ERR_INVALID_ARG, "null cache, input or output");
+  if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(q))
+    return fail(KVQ_ERR_INVALID_ARG, "cache, k_new, v_new and q must be 16-byte aligned");
   if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);

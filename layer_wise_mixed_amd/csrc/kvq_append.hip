@@ -13,7 +13,7 @@ namespace kvq {
 namespace {
 
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  __shared__ uint16_t xs[2][GS][D];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][GS][D];
   __shared__ uint16_t cs[2][GS][D];
   const LayerGeom& g = a.geo;
   const int tid = threadIdx.x;
@@ -32,19 +32,41 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   if (y < F) {
     const int m = m0 + y;
-    for (int idx = tid; idx < GS * D; idx += blockDim.x) {
-      const int i = idx >> 7, c = idx & 127;
-      const int t = GS * m + i;
-      uint16_t kv, vv;
-      if (t < L0) {  // earlier tokens of this group wait in the tail
-        kv = tail_get(tail, false, i, c);
-        vv = tail_get(tail, true, i, c);
-      } else {
-        kv = kn[(size_t)(t - L0) * D + c];
-        vv = vn[(size_t)(t - L0) * D + c];
+    if (GS * m >= L0) {
+      // the whole group is new: 32 contiguous rows of k_new and of v_new, 8 KiB
+      // each, copied in 16-byte pieces, all loads issued before any store
+      typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+      const u4_t* ks = (const u4_t*)(kn + (size_t)(GS * m - L0) * D);
+      const u4_t* vs = (const u4_t*)(vn + (size_t)(GS * m - L0) * D);
+      u4_t* kd = (u4_t*)&xs[0][0][0];
+      u4_t* vd = (u4_t*)&xs[1][0][0];
+      constexpr int kPieces = GS * D / 8;  // 512 per tensor
+      u4_t a[kPieces / 256], b[kPieces / 256];
+#pragma unroll
+      for (int q = 0; q < kPieces / 256; ++q) {
+        a[q] = ks[tid + 256 * q];
+        b[q] = vs[tid + 256 * q];
       }
-      xs[0][i][c] = kv;
-      xs[1][i][c] = vv;
+#pragma unroll
+      for (int q = 0; q < kPieces / 256; ++q) {
+        kd[tid + 256 * q] = a[q];
+        vd[tid + 256 * q] = b[q];
+      }
+    } else {
+      for (int idx = tid; idx < GS * D; idx += blockDim.x) {
+        const int i = idx >> 7, c = idx & 127;
+        const int t = GS * m + i;
+        uint16_t kv, vv;
+        if (t < L0) {  // earlier tokens of this group wait in the tail
+          kv = tail_get(tail, false, i, c);
+          vv = tail_get(tail, true, i, c);
+        } else {
+          kv = kn[(size_t)(t - L0) * D + c];
+          vv = vn[(size_t)(t - L0) * D + c];
+        }
+        xs[0][i][c] = kv;
+        xs[1][i][c] = vv;
+      }
     }
     __syncthreads();
     quantize_record(xs, cs, stream + (size_t)m * g.record_bytes, g.kb, g.vb, g.k_token, tid);
@@ -111,7 +133,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 // INT4 tokens that fall in it (TriAxialKV page, "Facts": leftover INT2
 // tokens take the INT4 per-token path).
 __global__ __launch_bounds__(256) void paged_append_kernel(AppendArgs a) {
-  __shared__ uint16_t xs[2][GS][D];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][GS][D];
   __shared__ uint16_t cs[2][GS][D];
   const LayerGeom& g = a.geo;
   const PagedGeom& pg = a.pg;

@@ -228,3 +228,16 @@ def test_paged_auto_splits_hold_the_limits(batch, max_seq_len):
     assert 2 <= s <= 1024
     assert -(-groups // (s - 1)) <= 256
     assert kvq.workspace_bytes(plan, batch, max_seq_len) == batch * 32 * s * 129 * 4
+
+
+def test_misaligned_pointers_are_rejected(lib):
+    plan = kvq.plan_layers(kvq.make_shape(32, 8, 4, max_tokens=256), [(8, 4)])
+    P = ctypes.byref(plan)
+    f, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+    assert lib.kvq_quantize_append(P, 0, f, odd, f, f, 2, 3, None, None) == kvq.ERR_INVALID_ARG
+    assert "16-byte" in lib.kvq_last_error().decode()
+    assert lib.kvq_quantize_append(P, 0, odd, f, f, f, 2, 3, None, None) == kvq.ERR_INVALID_ARG
+    assert lib.kvq_decode_attention(P, 0, f, odd, f, 2, 64, ctypes.c_float(0.088), f, 0, None, f, 1 << 30, 0,
+                                    None, None) == kvq.ERR_INVALID_ARG
+    assert lib.kvq_append_decode_attention(P, 0, f, f, odd, f, f, 2, 64, ctypes.c_float(0.088), f, 0, None, f,
+                                           1 << 30, 0, None) == kvq.ERR_INVALID_ARG
