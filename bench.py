@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 import synthetic as syn  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak
 METRIC = "decode-attention tokens/s and effective HBM GB/s (% of peak), batch 64, 1 GPU"
 
 
@@ -165,6 +166,47 @@ class Workload:
         nbytes = streams * self.P * 128 * 2 * 2 + streams * ((self.P // 32) * lp.record_bytes + (self.P % 32) * 512)
         return {"layer": li, "format": f"K{lp.k_bits}V{lp.v_bits}", "tokens": self.B * self.P, "us": t * 1e6,
                 "bytes": nbytes, "GBps": nbytes / t / 1e9, "frac": nbytes / t / 1e9 / HBM_PEAK_GBS}
+
+    def prefix_attention_rate(self, requests=4, chunk=256, reps=3):
+        """Chunked prefill against the cache: `chunk` query tokens of each of the first
+        `requests` requests attend over the first layer's cached prefix (P tokens) in one
+        prefix-attention call; HIP events bound to the split pass time `reps` calls after one
+        untimed call (timing only: by now the tail slots may hold later decode tokens). FLOPs:
+        the two products, 2 * 2 * rows * P * 128, rows = requests * chunk * Hq."""
+        import torch
+
+        kvq = self.kvq
+        li = self.layer_ids[0]
+        nb = min(requests, self.B)
+        q = syn.queries_steps_fp16(self.seed, li, nb, self.Hq, self.P, chunk, device="cuda")
+        q = q.permute(0, 2, 1, 3).contiguous()
+        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        wsb = kvq.prefix_workspace_bytes(self.plan, nb, chunk, self.P)
+        ws = torch.empty(wsb // 4 + 1, dtype=torch.float32, device="cuda") if wsb else None
+        lens = torch.full((nb,), self.P, dtype=torch.int32, device="cuda")
+
+        def call():
+            kvq.prefix_attention(self.plan, 0, self.cache, q, lens, self.P, self.scale, out, lse, ws)
+
+        call()
+        torch.cuda.synchronize()
+        kvq.timer_start(reps)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        ms, n = kvq.timer_read(kvq.TIMER_PREFIX)
+        mms, mn = kvq.timer_read(kvq.TIMER_MERGE)
+        kvq.timer_stop()
+        t = ms / 1e3 / max(n, 1)
+        tm = mms / 1e3 / max(mn, 1) if mn else 0.0
+        rows = nb * chunk * self.Hq
+        flops = 4.0 * rows * self.P * 128
+        lp = self.plan.layers[0]
+        return {"layer": li, "format": f"K{lp.k_bits}V{lp.v_bits}", "requests": nb, "chunk": chunk,
+                "prefix": self.P, "rows": rows, "us": t * 1e6, "merge_us": tm * 1e6, "flops": flops,
+                "TFLOPs": flops / t / 1e12, "bound": "mfma", "peak_TFLOPs": MFMA_F16_PEAK_TFLOPS,
+                "frac": flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS}
 
     def reset(self):
         self.lens_before.copy_(self.lens_base)
@@ -580,6 +622,12 @@ def main():
         print(f"# prefill append, layer {result['prefill_append']['layer']}: "
               f"{result['prefill_append']['us']:.1f} us, {result['prefill_append']['GBps']:.0f} GB/s", file=sys.stderr,
               flush=True)
+    if hasattr(wl, "prefix_attention_rate"):
+        # chunked-prefill attention over the quantized prefix (matrix-core bound), beside the step
+        pa = result["prefix_attention"] = wl.prefix_attention_rate()
+        print(f"# prefix attention, layer {pa['layer']} {pa['format']}: {pa['rows']} rows x {pa['prefix']} tokens "
+              f"in {pa['us']:.1f} us, {pa['TFLOPs']:.0f} TFLOP/s ({100 * pa['frac']:.1f}% of fp16 peak)",
+              file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -253,6 +253,44 @@ int kvq_append_decode_attention(const kvq_plan *plan, int32_t layer, void *cache
                                 void *workspace, size_t workspace_bytes, int32_t num_splits,
                                 kvq_stream_t stream);
 
+/* Workspace bytes kvq_prefix_attention needs: 0 when it uses one split, else
+ * batch * chunk * Hq * splits * (128 + 1) fp32. num_splits = 0 means the
+ * count the library would choose. Returns 0 on invalid arguments too. */
+size_t kvq_prefix_workspace_bytes(const kvq_plan *plan, int32_t batch, int32_t chunk,
+                                  int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * kvq_prefix_attention -- chunked prefill against a quantized cache: softmax
+ * attention of a chunk of new query tokens over every token already cached
+ * for the request (the prefix: packed groups and fp16 tail, as stored), with
+ * no mask, since the whole prefix precedes the chunk. Its (out, lse) is the
+ * prefix part of the chunk's attention; the chunk's own causal part (its
+ * fp16 K and V, which kvq_quantize_append then stores) merges with it by
+ * log-sum-exp: o = (e^lse_p o_p + e^lse_c o_c) / (e^lse_p + e^lse_c). The
+ * keys and values are dequantized in registers exactly as by
+ * kvq_decode_attention (asymmetric groupwise codes, per-channel or
+ * per-token keys, per-token values: KIVI and KVTuner summary pages), and
+ * the prefix may be split as in flash decoding (TriAxialKV page, "Facts":
+ * splits merged by online log-sum-exp).
+ *   q: device fp16 [batch][chunk][Hq][128], the chunk's queries;
+ *   chunk: query tokens a request (the same for every request), >= 0;
+ *   seq_lens: device [batch] cached tokens per request (the prefix length);
+ *   max_seq_len: host upper bound of seq_lens;
+ *   out: device fp32 [batch][chunk][Hq][128];
+ *   lse_out: device fp32 [batch][chunk][Hq] natural-log log-sum-exp,
+ *     nullable; a request with an empty prefix gets out = 0, lse = -inf;
+ *   workspace: device, kvq_prefix_workspace_bytes(...) bytes (may be NULL
+ *     when that is 0); num_splits: 0 = automatic, else 1..1024.
+ * Query head h of a token uses KV head h / (Hq / Hkv). Contiguous plans only.
+ *   Errors: INVALID_ARG (batch * chunk * Hq > 2^26 included), UNSUPPORTED (paged
+ *   plan), CAPACITY (max_seq_len > max_tokens), WORKSPACE, HIP.
+ */
+int kvq_prefix_attention(const kvq_plan *plan, int32_t layer, const void *cache,
+                         const uint16_t *q, int32_t chunk, const int32_t *seq_lens,
+                         int32_t batch, int32_t max_seq_len, float softmax_scale, float *out,
+                         float *lse_out, void *workspace, size_t workspace_bytes,
+                         int32_t num_splits, kvq_stream_t stream);
+
 /*
  * kvq_dequantize -- the cache of one layer back in fp32, for checking:
  * k_out, v_out: device fp32 [batch][Hkv][max_seq_len][128]; token j of
@@ -277,7 +315,8 @@ const char *kvq_last_error(void);
  * the launch stream). kvq_timer_start(capacity) clears and arms it for up to
  * `capacity` launches per kind; kvq_timer_read(kind, ...) synchronizes the
  * recorded events and returns the summed milliseconds and the launch count
- * for a kind (0 = append, 1 = decode split pass, 2 = merge pass);
+ * for a kind (0 = append, 1 = decode split pass, 2 = merge pass, 3 = prefix
+ * split pass);
  * kvq_timer_stop() disarms it and frees the events.
  */
 int kvq_timer_start(int32_t capacity);

@@ -26,7 +26,7 @@ AXIS_CHANNEL = 0
 AXIS_TOKEN = 1
 OUT_F16 = 0
 OUT_F32 = 1
-TIMER_APPEND, TIMER_SPLIT, TIMER_MERGE = 0, 1, 2
+TIMER_APPEND, TIMER_SPLIT, TIMER_MERGE, TIMER_PREFIX = 0, 1, 2, 3
 
 
 class KvqError(RuntimeError):
@@ -71,8 +71,9 @@ class Pages(ctypes.Structure):
 
 
 SYMBOLS = ["kvq_plan_layers", "kvq_quantize_append", "kvq_decode_workspace_bytes", "kvq_decode_num_splits",
-           "kvq_decode_attention", "kvq_append_decode_attention", "kvq_dequantize", "kvq_last_error",
-           "kvq_timer_start", "kvq_timer_read", "kvq_timer_stop"]
+           "kvq_decode_attention", "kvq_append_decode_attention", "kvq_prefix_workspace_bytes",
+           "kvq_prefix_attention", "kvq_dequantize", "kvq_last_error", "kvq_timer_start", "kvq_timer_read",
+           "kvq_timer_stop"]
 
 _lib = None
 
@@ -101,6 +102,11 @@ def load():
     L.kvq_append_decode_attention.argtypes = [ctypes.POINTER(Plan), i32, P, P, P, P, P, i32, i32, ctypes.c_float,
                                               P, i32, P, P, ctypes.c_size_t, i32, P]
     L.kvq_append_decode_attention.restype = ctypes.c_int
+    L.kvq_prefix_workspace_bytes.argtypes = [ctypes.POINTER(Plan), i32, i32, i32, i32]
+    L.kvq_prefix_workspace_bytes.restype = ctypes.c_size_t
+    L.kvq_prefix_attention.argtypes = [ctypes.POINTER(Plan), i32, P, P, i32, P, i32, i32, ctypes.c_float, P, P, P,
+                                       ctypes.c_size_t, i32, P]
+    L.kvq_prefix_attention.restype = ctypes.c_int
     L.kvq_dequantize.argtypes = [ctypes.POINTER(Plan), i32, P, P, i32, i32, P, P, ctypes.POINTER(Pages), P]
     L.kvq_dequantize.restype = ctypes.c_int
     L.kvq_last_error.argtypes = []
@@ -222,6 +228,28 @@ def append_decode_attention(plan: Plan, layer: int, cache, k_new, v_new, q, seq_
                                               _ptr(q), _ptr(seq_lens), batch, max_seq_len, float(softmax_scale),
                                               _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
                                               _ptr(lse), _ptr(workspace), ws_bytes, num_splits, _stream(stream)))
+
+
+def prefix_workspace_bytes(plan: Plan, batch: int, chunk: int, max_seq_len: int, num_splits: int = 0) -> int:
+    return int(load().kvq_prefix_workspace_bytes(ctypes.byref(plan), batch, chunk, max_seq_len, num_splits))
+
+
+def prefix_attention(plan: Plan, layer: int, cache, q, seq_lens, max_seq_len: int, softmax_scale: float, out,
+                     lse=None, workspace=None, num_splits: int = 0, stream=None):
+    """Attention of a chunk of query tokens over each request's cached prefix (no mask).
+    q: fp16 [batch, chunk, Hq, 128]; seq_lens: cached tokens per request; out: fp32 [batch, chunk, Hq, 128];
+    lse: fp32 [batch, chunk, Hq] or None; workspace: prefix_workspace_bytes(...) bytes (None if 0)."""
+    import torch
+
+    assert q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 4
+    assert out.dtype == torch.float32 and out.is_contiguous() and out.shape == q.shape
+    assert lse is None or (lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:3])
+    batch, chunk = q.shape[0], q.shape[1]
+    _dev_i32(seq_lens, batch, "seq_lens")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().kvq_prefix_attention(ctypes.byref(plan), layer, _ptr(cache), _ptr(q), chunk, _ptr(seq_lens), batch,
+                                       max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       ws_bytes, num_splits, _stream(stream)))
 
 
 def dequantize(plan: Plan, layer: int, cache, seq_lens, batch: int, max_seq_len: int, k_out, v_out,

@@ -39,12 +39,15 @@ uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- timer
 
+// 0 = append, 1 = decode split pass, 2 = merge pass, 3 = prefix split pass
+constexpr int kTimerKinds = 4;
+
 struct Timer {
   std::mutex mu;
   bool armed = false;
   int capacity = 0;
-  std::vector<hipEvent_t> ev[3][2];
-  int used[3] = {0, 0, 0};
+  std::vector<hipEvent_t> ev[kTimerKinds][2];
+  int used[kTimerKinds] = {};
 } g_timer;
 
 void timer_free_locked() {
@@ -55,7 +58,7 @@ void timer_free_locked() {
     }
   g_timer.armed = false;
   g_timer.capacity = 0;
-  for (int k = 0; k < 3; ++k) g_timer.used[k] = 0;
+  for (int k = 0; k < kTimerKinds; ++k) g_timer.used[k] = 0;
 }
 
 // Event pair for the next launch of `kind` if the timer is armed and has room.
@@ -170,6 +173,22 @@ int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   if (s > 1024) s = 1024;
+  return (int32_t)s;
+}
+
+// Prefix attention: the row tiles already give batch * Hkv * tiles
+// workgroups; split the prefix only while that is under ~512, keeping at
+// least 8 groups in each split.
+int32_t prefix_splits(const kvq_plan* plan, int32_t batch, int32_t chunk, int32_t max_seq_len) {
+  const int64_t g = plan->shape.num_q_heads / plan->shape.num_kv_heads;
+  const int64_t tp = 16 / g;
+  const int64_t wgs = (int64_t)batch * plan->shape.num_kv_heads * ((chunk + tp - 1) / tp);
+  const int64_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
+  if (nvg <= 0 || wgs <= 0) return 1;
+  int64_t s = (512 + wgs - 1) / wgs;
+  const int64_t max_s = nvg / 8 > 1 ? nvg / 8 : 1;
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
   return (int32_t)s;
 }
 
@@ -431,6 +450,77 @@ int kvq_append_decode_attention(const kvq_plan* plan, int32_t layer, void* cache
   return hip_status(e, "merge launch");
 }
 
+size_t kvq_prefix_workspace_bytes(const kvq_plan* plan, int32_t batch, int32_t chunk, int32_t max_seq_len,
+                                  int32_t num_splits) {
+  if (!plan || batch < 0 || chunk < 0 || max_seq_len < 0 || num_splits < 0 || num_splits > 1024) return 0;
+  const int32_t s = num_splits ? num_splits : prefix_splits(plan, batch, chunk, max_seq_len);
+  if (s == 1) return 0;
+  return (size_t)batch * chunk * plan->shape.num_q_heads * s * (kvq::D + 1) * sizeof(float);
+}
+
+int kvq_prefix_attention(const kvq_plan* plan, int32_t layer, const void* cache, const uint16_t* q, int32_t chunk,
+                         const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float softmax_scale,
+                         float* out, float* lse_out, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                         kvq_stream_t stream) {
+  int st = check_plan_layer(plan, layer);
+  if (st) return st;
+  if (is_paged(plan)) return fail(KVQ_ERR_UNSUPPORTED, "prefix attention reads contiguous streams only");
+  if (!cache || !q || !out || !seq_lens) return fail(KVQ_ERR_INVALID_ARG, "null cache, q, seq_lens or out");
+  if (!aligned16(cache) || !aligned16(q)) return fail(KVQ_ERR_INVALID_ARG, "cache and q must be 16-byte aligned");
+  if (batch < 0 || batch > plan->shape.max_batch)
+    return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
+  if (chunk < 0 || (int64_t)batch * chunk * plan->shape.num_q_heads > (1 << 26))
+    return fail(KVQ_ERR_INVALID_ARG, "chunk %d: batch * chunk * Hq rows must be at most 2^26", chunk);
+  if (num_splits < 0 || num_splits > 1024) return fail(KVQ_ERR_INVALID_ARG, "num_splits %d", num_splits);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+  if (max_seq_len > capacity_tokens(plan, nullptr))
+    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > %lld tokens of capacity", max_seq_len,
+                (long long)capacity_tokens(plan, nullptr));
+  if (batch == 0 || chunk == 0) return ok();
+  const int32_t splits = num_splits ? num_splits : prefix_splits(plan, batch, chunk, max_seq_len);
+  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
+  const int32_t gps = (nvg + splits - 1) / splits;
+  const size_t rows = (size_t)batch * chunk * plan->shape.num_q_heads;
+  const size_t need = splits > 1 ? rows * splits * (kvq::D + 1) * sizeof(float) : 0;
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  const int64_t tp = 16 / (plan->shape.num_q_heads / plan->shape.num_kv_heads);
+  if ((int64_t)splits * ((chunk + tp - 1) / tp) > 0x7FFFFFFF)
+    return fail(KVQ_ERR_INVALID_ARG, "num_splits %d times the row tiles exceeds the grid", splits);
+  kvq::DecodeArgs a;
+  a.geo = geom(plan, layer, cache);
+  a.pg = paged_geom(plan, layer, nullptr);
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.splits = splits;
+  a.groups_per_split = gps;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.part_o = (float*)workspace;
+  a.part_lse = need ? a.part_o + rows * splits * kvq::D : nullptr;
+  a.out = out;
+  a.out_f32 = 1;
+  a.lse_out = lse_out;
+  a.chunk = chunk;
+  hipStream_t s = (hipStream_t)stream;
+  kvq::EventPair ev;
+  bool timed = timer_slot(3, &ev);
+  hipError_t e = kvq::launch_prefix_split_mfma(a, batch, s, timed ? &ev : nullptr);
+  if (e != hipSuccess) return hip_status(e, "prefix split launch");
+  if (splits == 1) return ok();
+  kvq::MergeArgs m;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.splits = splits;
+  m.rows = (int)rows;
+  m.out = out;
+  m.out_f32 = 1;
+  m.lse_out = lse_out;
+  timed = timer_slot(2, &ev);
+  e = kvq::launch_merge(m, s, timed ? &ev : nullptr);
+  return hip_status(e, "merge launch");
+}
+
 int kvq_dequantize(const kvq_plan* plan, int32_t layer, const void* cache, const int32_t* seq_lens, int32_t batch,
                    int32_t max_seq_len, float* k_out, float* v_out, const kvq_pages* pages, kvq_stream_t stream) {
   int st = check_plan_layer(plan, layer);
@@ -461,7 +551,7 @@ int kvq_timer_start(int32_t capacity) {
   if (capacity <= 0 || capacity > (1 << 20)) return fail(KVQ_ERR_INVALID_ARG, "timer capacity %d", capacity);
   std::lock_guard<std::mutex> lk(g_timer.mu);
   timer_free_locked();
-  for (int k = 0; k < 3; ++k)
+  for (int k = 0; k < kTimerKinds; ++k)
     for (int i = 0; i < 2; ++i) {
       g_timer.ev[k][i].resize(capacity);
       for (int n = 0; n < capacity; ++n) {
@@ -479,7 +569,8 @@ int kvq_timer_start(int32_t capacity) {
 }
 
 int kvq_timer_read(int32_t kind, double* total_ms, int32_t* launches) {
-  if (kind < 0 || kind > 2 || !total_ms || !launches) return fail(KVQ_ERR_INVALID_ARG, "bad timer read arguments");
+  if (kind < 0 || kind >= kTimerKinds || !total_ms || !launches)
+    return fail(KVQ_ERR_INVALID_ARG, "bad timer read arguments");
   std::lock_guard<std::mutex> lk(g_timer.mu);
   double sum = 0.0;
   const int n = g_timer.used[kind];

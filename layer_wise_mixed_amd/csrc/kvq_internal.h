@@ -189,6 +189,9 @@ struct DecodeArgs {
   // a plain decode.
   const uint16_t* k_new = nullptr;
   const uint16_t* v_new = nullptr;
+  // Prefix attention: q holds `chunk` tokens a request, [batch][chunk][Hq][128],
+  // and the rows of out, lse and the partials follow that order.
+  int chunk = 0;
 };
 
 struct MergeArgs {
@@ -211,6 +214,7 @@ hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const Ev
 hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s);
 hipError_t launch_decode_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_decode_paged(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
+hipError_t launch_prefix_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_append_paged(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, const EventPair* ev);

@@ -16,6 +16,10 @@ Functions and the passages they follow:
   attention           -- softmax attention of a decode query, fp64
   lse_merge           -- split merge by log-sum-exp (TriAxialKV page,
                          "Facts": split decode bullet)
+  chunk_prefill       -- a prefill chunk's attention over the quantized
+                         prefix plus its own fp16 tokens, causally (the
+                         chunked-prefill reading: the prefix is what the
+                         cache stores, the chunk is not yet quantized)
   pack_stream / unpack_stream -- this project's byte layout of the cache
   quantize_tokens / pack_paged / unpack_paged / decode_paged -- the paged
                          INT2/INT4 pool (TriAxialKV page, "Facts": page-pool,
@@ -343,6 +347,29 @@ def decode_stream(q_fp16, k_fp16, v_fp16, kb: int, vb: int, k_token: bool, scale
     sq = quantize_stream(k_fp16, v_fp16, kb, vb, k_token)
     kd, vd = dequant_stream(sq)
     return attention(q_fp16, kd, vd, scale)
+
+
+def chunk_prefill(q_fp16, k_prefix, v_prefix, k_chunk, v_chunk, kb: int, vb: int, k_token: bool, scale: float):
+    """Attention of a prefill chunk with a quantized cache in front of it: the
+    query rows of chunk token i (q [C, G, D]) attend to the prefix as the cache
+    stores it (k_prefix/v_prefix fp16 [L, D], quantized as by quantize_stream,
+    the tail kept fp16) and, causally, to the chunk's own fp16 tokens 0..i
+    (k_chunk/v_chunk [C, D]). One softmax over all those keys, fp64: (out
+    [C, G, D], lse [C, G])."""
+    q = _u16(q_fp16).reshape(len(k_chunk), -1, D)
+    C, G = q.shape[0], q.shape[1]
+    kp = vp = np.zeros((0, D), np.float32)
+    if len(k_prefix):
+        kp, vp = dequant_stream(quantize_stream(k_prefix, v_prefix, kb, vb, k_token))
+    kc = _u16(k_chunk).reshape(C, D).view(np.float16).astype(np.float32)
+    vc = _u16(v_chunk).reshape(C, D).view(np.float16).astype(np.float32)
+    out = np.zeros((C, G, D))
+    lse = np.zeros((C, G))
+    for i in range(C):
+        keys = np.concatenate([kp, kc[:i + 1]])
+        vals = np.concatenate([vp, vc[:i + 1]])
+        out[i], lse[i] = attention(q[i], keys, vals, scale)
+    return out, lse
 
 
 def decode_packed(cache_layer: np.ndarray, stream_stride: int, stream_ids, lens, kb, vb, k_token,

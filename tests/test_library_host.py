@@ -241,3 +241,41 @@ def test_misaligned_pointers_are_rejected(lib):
                                     None, None) == kvq.ERR_INVALID_ARG
     assert lib.kvq_append_decode_attention(P, 0, f, f, odd, f, f, 2, 64, ctypes.c_float(0.088), f, 0, None, f,
                                            1 << 30, 0, None) == kvq.ERR_INVALID_ARG
+
+
+def test_prefix_attention_argument_errors(lib):
+    plan = kvq.plan_layers(kvq.make_shape(32, 8, 4, max_tokens=256), [(8, 4)] * 2)
+    f, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+
+    def call(plan=plan, layer=0, batch=2, chunk=64, max_seq_len=200, ws_bytes=1 << 30, splits=0, seq=True, q=f,
+             ws=True):
+        return lib.kvq_prefix_attention(ctypes.byref(plan), layer, f, q, chunk, f if seq else None, batch,
+                                        max_seq_len, ctypes.c_float(0.088), f, None, f if ws else None, ws_bytes,
+                                        splits, None)
+
+    assert call(layer=2) == kvq.ERR_INVALID_ARG
+    assert call(batch=5) == kvq.ERR_INVALID_ARG
+    assert call(chunk=-1) == kvq.ERR_INVALID_ARG
+    assert call(batch=4, chunk=1 << 20) == kvq.ERR_INVALID_ARG  # 4 * 2^20 * 32 rows > 2^26
+    assert call(max_seq_len=257) == kvq.ERR_CAPACITY
+    assert call(max_seq_len=-1) == kvq.ERR_INVALID_ARG
+    assert call(splits=2000) == kvq.ERR_INVALID_ARG
+    assert call(splits=3, ws_bytes=16) == kvq.ERR_WORKSPACE
+    assert call(splits=3, ws=False) == kvq.ERR_WORKSPACE
+    assert call(seq=False) == kvq.ERR_INVALID_ARG
+    assert call(q=odd) == kvq.ERR_INVALID_ARG
+    assert "16-byte" in lib.kvq_last_error().decode()
+    assert call(plan=_paged_plan()) == kvq.ERR_UNSUPPORTED
+    assert call(batch=0) == kvq.OK and call(chunk=0) == kvq.OK  # nothing to do
+
+
+def test_prefix_workspace_and_auto_splits():
+    plan = kvq.plan_layers(kvq.make_shape(32, 8, 4, max_tokens=4096), [(4, 2)])
+    # 2 requests x 8 KV heads x 64 row tiles (256 tokens, 4 a tile) fill the chip: one split
+    assert kvq.prefix_workspace_bytes(plan, 2, 256, 4096) == 0
+    # one 4-token chunk: 8 workgroups, so the prefix is split, into 16 splits of 8 groups (a
+    # split keeps at least 8 of the 128)
+    assert kvq.prefix_workspace_bytes(plan, 1, 4, 4096) == 1 * 4 * 32 * 16 * 129 * 4
+    assert kvq.prefix_workspace_bytes(plan, 1, 4, 4096, 5) == 4 * 32 * 5 * 129 * 4
+    assert kvq.prefix_workspace_bytes(plan, 1, 4, 4096, 1) == 0
+    assert kvq.prefix_workspace_bytes(plan, 1, 4, 100) == 0  # 4 groups: no more than one split
