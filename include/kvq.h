@@ -266,12 +266,12 @@ size_t kvq_prefix_workspace_bytes(const kvq_plan *plan, int32_t batch, int32_t c
  * no mask, since the whole prefix precedes the chunk. Its (out, lse) is the
  * prefix part of the chunk's attention; the chunk's own causal part (its
  * fp16 K and V, which kvq_quantize_append then stores) merges with it by
- * log-sum-exp: o = (e^lse_p o_p + e^lse_c o_c) / (e^lse_p + e^lse_c). The
- * keys and values are dequantized in registers exactly as by
- * kvq_decode_attention (asymmetric groupwise codes, per-channel or
- * per-token keys, per-token values: KIVI and KVTuner summary pages), and
- * the prefix may be split as in flash decoding (TriAxialKV page, "Facts":
- * splits merged by online log-sum-exp).
+ * log-sum-exp: o = (e^lse_p o_p + e^lse_c o_c) / (e^lse_p + e^lse_c). Each
+ * packed group is dequantized once per 256 query rows (fmaf(code, scale,
+ * zero) as in kvq_dequantize: asymmetric groupwise codes, per-channel or
+ * per-token keys, per-token values, KIVI and KVTuner summary pages) and
+ * multiplied on the matrix cores; the prefix may be split as in flash
+ * decoding (TriAxialKV page, "Facts": splits merged by online log-sum-exp).
  *   q: device fp16 [batch][chunk][Hq][128], the chunk's queries;
  *   chunk: query tokens a request (the same for every request), >= 0;
  *   seq_lens: device [batch] cached tokens per request (the prefix length);
@@ -280,7 +280,8 @@ size_t kvq_prefix_workspace_bytes(const kvq_plan *plan, int32_t batch, int32_t c
  *   lse_out: device fp32 [batch][chunk][Hq] natural-log log-sum-exp,
  *     nullable; a request with an empty prefix gets out = 0, lse = -inf;
  *   workspace: device, kvq_prefix_workspace_bytes(...) bytes (may be NULL
- *     when that is 0); num_splits: 0 = automatic, else 1..1024.
+ *     when that is 0); num_splits: 0 = automatic, else 1..1024;
+ *   cache, q, out and workspace 16-byte aligned.
  * Query head h of a token uses KV head h / (Hq / Hkv). Contiguous plans only.
  *   Errors: INVALID_ARG (batch * chunk * Hq > 2^26 included), UNSUPPORTED (paged
  *   plan), CAPACITY (max_seq_len > max_tokens), WORKSPACE, HIP.

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_split_mfma.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_split_mfma.hip", "kvq_prefix.hip"]
 ARCH = "gfx950"
 
 

@@ -176,13 +176,16 @@ int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
   return (int32_t)s;
 }
 
-// Prefix attention: the row tiles already give batch * Hkv * tiles
+// Prefix attention: the row blocks already give batch * Hkv * blocks
 // workgroups; split the prefix only while that is under ~512, keeping at
 // least 8 groups in each split.
+int64_t prefix_blocks(const kvq_plan* plan, int32_t chunk) {
+  const int64_t rows = (int64_t)chunk * (plan->shape.num_q_heads / plan->shape.num_kv_heads);
+  return (rows + kvq::prefix_rows_per_block() - 1) / kvq::prefix_rows_per_block();
+}
+
 int32_t prefix_splits(const kvq_plan* plan, int32_t batch, int32_t chunk, int32_t max_seq_len) {
-  const int64_t g = plan->shape.num_q_heads / plan->shape.num_kv_heads;
-  const int64_t tp = 16 / g;
-  const int64_t wgs = (int64_t)batch * plan->shape.num_kv_heads * ((chunk + tp - 1) / tp);
+  const int64_t wgs = (int64_t)batch * plan->shape.num_kv_heads * prefix_blocks(plan, chunk);
   const int64_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
   if (nvg <= 0 || wgs <= 0) return 1;
   int64_t s = (512 + wgs - 1) / wgs;
@@ -466,7 +469,8 @@ int kvq_prefix_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   if (st) return st;
   if (is_paged(plan)) return fail(KVQ_ERR_UNSUPPORTED, "prefix attention reads contiguous streams only");
   if (!cache || !q || !out || !seq_lens) return fail(KVQ_ERR_INVALID_ARG, "null cache, q, seq_lens or out");
-  if (!aligned16(cache) || !aligned16(q)) return fail(KVQ_ERR_INVALID_ARG, "cache and q must be 16-byte aligned");
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || !aligned16(workspace))
+    return fail(KVQ_ERR_INVALID_ARG, "cache, q, out and workspace must be 16-byte aligned");
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
   if (chunk < 0 || (int64_t)batch * chunk * plan->shape.num_q_heads > (1 << 26))
@@ -485,9 +489,8 @@ int kvq_prefix_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   const size_t need = splits > 1 ? rows * splits * (kvq::D + 1) * sizeof(float) : 0;
   if (need && (!workspace || workspace_bytes < need))
     return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  const int64_t tp = 16 / (plan->shape.num_q_heads / plan->shape.num_kv_heads);
-  if ((int64_t)splits * ((chunk + tp - 1) / tp) > 0x7FFFFFFF)
-    return fail(KVQ_ERR_INVALID_ARG, "num_splits %d times the row tiles exceeds the grid", splits);
+  if ((int64_t)splits * prefix_blocks(plan, chunk) > 0x7FFFFFFF)
+    return fail(KVQ_ERR_INVALID_ARG, "num_splits %d times the row blocks exceeds the grid", splits);
   kvq::DecodeArgs a;
   a.geo = geom(plan, layer, cache);
   a.pg = paged_geom(plan, layer, nullptr);
@@ -505,7 +508,7 @@ int kvq_prefix_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   hipStream_t s = (hipStream_t)stream;
   kvq::EventPair ev;
   bool timed = timer_slot(3, &ev);
-  hipError_t e = kvq::launch_prefix_split_mfma(a, batch, s, timed ? &ev : nullptr);
+  hipError_t e = kvq::launch_prefix(a, batch, s, timed ? &ev : nullptr);
   if (e != hipSuccess) return hip_status(e, "prefix split launch");
   if (splits == 1) return ok();
   kvq::MergeArgs m;

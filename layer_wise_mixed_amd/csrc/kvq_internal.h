@@ -190,7 +190,7 @@ struct DecodeArgs {
   const uint16_t* k_new = nullptr;
   const uint16_t* v_new = nullptr;
   // Prefix attention: q holds `chunk` tokens a request, [batch][chunk][Hq][128],
-  // and the rows of out, lse and the partials follow that order.
+  // and the rows of out (fp32), lse and the partials follow that order.
   int chunk = 0;
 };
 
@@ -214,7 +214,8 @@ hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const Ev
 hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s);
 hipError_t launch_decode_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_decode_paged(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
-hipError_t launch_prefix_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
+hipError_t launch_prefix(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
+int prefix_rows_per_block();  // query rows one prefix-attention workgroup takes
 hipError_t launch_append_paged(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, const EventPair* ev);

@@ -362,32 +362,20 @@ struct alignas(16) SplitSmem {
   float q[kMaxG][D];  // q' of the G query rows (every wave writes the same values)
 };
 
-// The query rows of a workgroup: row i reads q at ptr(i) and writes output
-// row out(i). Decode: the G query heads of one KV head, consecutive rows.
+// The query rows of a workgroup, the G query heads of one KV head
+// (consecutive rows): row i reads q at ptr(i) and writes output row out(i).
 struct HeadRows {
-  static constexpr bool kContig = true;
   const uint16_t* q;
   size_t row0;
   __device__ __forceinline__ size_t out(int i) const { return row0 + i; }
   __device__ __forceinline__ const uint16_t* ptr(int i) const { return q + (row0 + i) * D; }
 };
 
-// Prefix attention: 16 / G consecutive chunk tokens times the G query heads
-// of KV head h; q and the outputs are [token][Hq] rows.
-struct ChunkRows {
-  static constexpr bool kContig = false;
-  const uint16_t* q;
-  size_t tok0;  // r * chunk + the tile's first token
-  int hq, g, h;
-  __device__ __forceinline__ size_t out(int i) const { return (tok0 + i / g) * hq + h * g + i % g; }
-  __device__ __forceinline__ const uint16_t* ptr(int i) const { return q + out(i) * D; }
-};
-
 // The lane's roles, q' = q * softmax_scale * log2(e) of the G rows into LDS,
 // and (per-token keys) the sums of q' over each 32-channel group. Every wave
 // writes all of q' (the same values), so no wave waits for another.
-template <int NS, bool QN, class Rows>
-__device__ __forceinline__ void setup_lane(const DecodeArgs& a, int G, const Rows& rows, float (*s_q)[D], Lane& ln,
+template <int NS, bool QN>
+__device__ __forceinline__ void setup_lane(const DecodeArgs& a, int G, const HeadRows& rows, float (*s_q)[D], Lane& ln,
                                            Acc& acc) {
   const int tid = threadIdx.x;
   ln.lane = tid & 63;
@@ -398,8 +386,7 @@ __device__ __forceinline__ void setup_lane(const DecodeArgs& a, int G, const Row
   ln.slot = c16 / G;
   ln.col_ok = ln.slot < NS;
   for (int c = ln.lane; c < G * (D / 8); c += 64) {  // 8 values a lane at a time
-    const uint16_t* src = Rows::kContig ? rows.ptr(0) + 8 * c : rows.ptr(c >> 4) + 8 * (c & 15);
-    const u4_t w = *(const u4_t*)src;
+    const u4_t w = *(const u4_t*)(rows.ptr(0) + 8 * c);
     const h8_t x = __builtin_bit_cast(h8_t, w);
     float* dst = &s_q[c >> 4][8 * (c & 15)];
     f4_t lo4, hi4;
@@ -437,8 +424,8 @@ __device__ __forceinline__ void setup_lane(const DecodeArgs& a, int G, const Row
 // output written: the final output when it is the only split, else the
 // split's partial (o, lse) for the merge pass. VB: the value code width the
 // wave's accumulators are in.
-template <int VB, int NS, int R, class Rows>
-__device__ __forceinline__ void finish(const DecodeArgs& a, const Rows& rows, int split, int wave, SplitSmem<R>& sm,
+template <int VB, int NS, int R>
+__device__ __forceinline__ void finish(const DecodeArgs& a, const HeadRows& rows, int split, int wave, SplitSmem<R>& sm,
                                        const Lane& ln, Acc& acc) {
   const int tid = threadIdx.x;
   const int G = ln.g;
@@ -836,49 +823,6 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   finish<VB, NS>(a, rows, split, wave, sm, ln, acc);
 }
 
-// Attention over a quantized prefix for a chunk of query tokens (chunked
-// prefill): every row of the chunk attends to all L cached tokens of its
-// request, and the result (o, lse) merges by log-sum-exp with the chunk's own
-// attention. The split pass above with 16-row tiles: a tile is 16 / G
-// consecutive chunk tokens times the G query heads of KV head h (NS = 1),
-// one workgroup per (split, tile, KV head, request), split fastest.
-template <int KB, int VB, bool KTOK>
-__global__ __launch_bounds__(256, 2) void prefix_mfma_kernel(DecodeArgs a) {
-  __shared__ SplitSmem<1> sm;
-  const LayerGeom& g = a.geo;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x % a.splits, tile = blockIdx.x / a.splits;
-  const int h = blockIdx.y, r = blockIdx.z;
-  const int tp = kMaxG / g.g;  // chunk tokens a tile
-  const int i0 = tile * tp;
-  const int nrows = min(tp, a.chunk - i0) * g.g;
-  const int L = min(max(a.seq_lens[r], 0), g.max_tokens);
-  const int nq = L / GS;
-  const int T = L - nq * GS;
-  const int nvg = nq + (T > 0);
-  const int g0 = split * a.groups_per_split;
-  const int g1 = min(g0 + a.groups_per_split, nvg);
-  uint8_t* stream = g.base + (size_t)(r * g.hkv + h) * g.stream_bytes;
-
-  Lane ln;
-  Acc acc;
-  float* kmeta = &sm.loop.kmeta[wave][0][0];
-  float* vmeta = sm.loop.vmeta[wave];
-  const int first = g0 + wave;
-  const int qend = min(g1, nq);
-  const int nk = first < qend ? (qend - first + kWaves - 1) / kWaves : 0;
-  StreamSrc<KB, VB> src;
-  src.first = stream + (size_t)first * g.record_bytes;
-  src.stride = (uint32_t)(kWaves * g.record_bytes);
-  src.parts = record_parts(KB, VB);
-  const ChunkRows rows{a.q, (size_t)r * a.chunk + i0, g.hq, g.g, h};
-  run_groups<KB, VB, KTOK, 1, 1>(src, nk, kmeta, vmeta, ln, acc,
-                                 [&] { setup_lane<1, KTOK && KB < 16>(a, nrows, rows, sm.q, ln, acc); });
-  if (T > 0 && nq >= g0 && nq < g1 && ((nq - g0) & (kWaves - 1)) == wave)
-    tail_pass<VB, 1>(stream + g.tail_offset, T, nullptr, nullptr, kmeta, vmeta, ln, acc);
-  finish<VB, 1>(a, rows, split, wave, sm, ln, acc);
-}
-
 // Paged pool: the splits of a request cover its INT2 groups first, then its
 // INT4 page pairs, each split of one kind only (TriAxialKV page, "Facts": the
 // page table puts INT2 pages first, so flash-decoding splits are
@@ -1004,26 +948,6 @@ hipError_t launch_k(const DecodeArgs& a, int batch, hipStream_t s, const EventPa
   }
 }
 
-template <int KB, int VB>
-hipError_t launch_prefix_kv(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
-  const int tiles = (a.chunk + kMaxG / a.geo.g - 1) / (kMaxG / a.geo.g);
-  const dim3 grid(a.splits * tiles, a.geo.hkv, batch), block(256);
-  if constexpr (KB < 16) {
-    if (a.geo.k_token) return launch_timed(prefix_mfma_kernel<KB, VB, true>, grid, block, s, ev, a);
-  }
-  return launch_timed(prefix_mfma_kernel<KB, VB, false>, grid, block, s, ev, a);
-}
-
-template <int KB>
-hipError_t launch_prefix_k(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
-  switch (a.geo.vb) {
-    case 2: return launch_prefix_kv<KB, 2>(a, batch, s, ev);
-    case 4: return launch_prefix_kv<KB, 4>(a, batch, s, ev);
-    case 8: return launch_prefix_kv<KB, 8>(a, batch, s, ev);
-    default: return launch_prefix_kv<KB, 16>(a, batch, s, ev);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_decode_paged(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
@@ -1040,15 +964,6 @@ hipError_t launch_decode_split_mfma(const DecodeArgs& a, int batch, hipStream_t 
     case 4: return launch_k<4>(a, batch, s, ev);
     case 8: return launch_k<8>(a, batch, s, ev);
     default: return launch_k<16>(a, batch, s, ev);
-  }
-}
-
-hipError_t launch_prefix_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
-  switch (a.geo.kb) {
-    case 2: return launch_prefix_k<2>(a, batch, s, ev);
-    case 4: return launch_prefix_k<4>(a, batch, s, ev);
-    case 8: return launch_prefix_k<8>(a, batch, s, ev);
-    default: return launch_prefix_k<16>(a, batch, s, ev);
   }
 }
 
