@@ -10,7 +10,9 @@ once per step position of the decode cycle.
 
 Prints one JSON line (the benchmark contract), with a roofline object for the
 split pass (algorithmic bytes per launch over its HIP-event duration) and a
-CPU baseline (the oracle, timed on a bounded sample of the same step).
+CPU baseline (the oracle, timed on a bounded sample of the same step). Beside
+the step, the line reports the append kernel at prefill size (HBM-bound) and
+the chunked-prefill attention over the quantized prefix (matrix-core bound).
 """
 from __future__ import annotations
 
@@ -206,7 +208,9 @@ class Workload:
         return {"layer": li, "format": f"K{lp.k_bits}V{lp.v_bits}", "requests": nb, "chunk": chunk,
                 "prefix": self.P, "rows": rows, "us": t * 1e6, "merge_us": tm * 1e6, "flops": flops,
                 "TFLOPs": flops / t / 1e12, "bound": "mfma", "peak_TFLOPs": MFMA_F16_PEAK_TFLOPS,
-                "frac": flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS}
+                "frac": flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                "TFLOPs_with_merge": flops / (t + tm) / 1e12,
+                "timing": "HIP events bound to the prefix kernel's dispatches (frac) and to the merge's"}
 
     def reset(self):
         self.lens_before.copy_(self.lens_base)
