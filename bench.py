@@ -357,9 +357,14 @@ class PagedWorkload:
         return per_layer * self.L
 
 
+# the kernel sources of the decode step (the prefix-attention kernel is not part of it)
+STEP_SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_internal.h", "kvq_quantize.h",
+                "kvq_split_mfma.hip"]
+
+
 def _source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "layer_wise_mixed_amd", "csrc"))):
+    for f in STEP_SOURCES:
         with open(os.path.join(ROOT, "layer_wise_mixed_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
