@@ -14,7 +14,7 @@ namespace {
 
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][GS][D];
-  __shared__ uint16_t cs[2][GS][D];
+  __shared__ uint16_t cs[2][GS][CS];
   const LayerGeom& g = a.geo;
   const int tid = threadIdx.x;
   const int y = blockIdx.x;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 // tokens take the INT4 per-token path).
 __global__ __launch_bounds__(256) void paged_append_kernel(AppendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][GS][D];
-  __shared__ uint16_t cs[2][GS][D];
+  __shared__ uint16_t cs[2][GS][CS];
   const LayerGeom& g = a.geo;
   const PagedGeom& pg = a.pg;
   const int tid = threadIdx.x;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void paged_append_kernel(AppendArgs a) {
     const int tensor = tid >> 6, p = (tid >> 2) & 15, n = tid & 3;
     if (p >= p_lo && p < p_hi) {
       float s, z;
-      quantize32(&xs[tensor][p][32 * n], 1, 4, &cs[tensor][p][32 * n], 1, &s, &z);
+      quantize32(&xs[tensor][p][32 * n], 1, 4, &cs[tensor][p][32 * n], 1, &s, &z, 2 * p);
       float* meta = (float*)(page + (tensor ? INT4_VMETA : INT4_KMETA));
       meta[16 * n + p] = s;
       meta[64 + 16 * n + p] = z;

@@ -29,13 +29,21 @@ __device__ inline void tail_put(uint8_t* rec, bool is_v, int j, int c, uint16_t 
   *(uint16_t*)(blk + word_offset(lane, e >> 1) + (e & 1) * 2) = x;
 }
 
-// One group of 32 values x[i * stride]; writes codes[i * cstride], returns scale/zero.
+// LDS row stride (uint16) of the code staging: 65 words, so that a wave's
+// per-token groups (rows j, column blocks 32n) and the packer's reads of 16
+// rows at once fall into different LDS banks.
+constexpr int CS = D + 2;
+
+// One group of 32 values x[i * stride]; writes codes[i * cstride], returns
+// scale/zero. The elements are visited from position rot on (mod 32): a lane
+// that starts elsewhere than its neighbours reads another LDS bank (the
+// result does not depend on the order).
 __device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint16_t* codes,
-                                  int cstride, float* scale, float* zero) {
+                                  int cstride, float* scale, float* zero, int rot = 0) {
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll 8
   for (int i = 0; i < GS; ++i) {
-    const float v = h2f(x[i * stride]);
+    const float v = h2f(x[((i + rot) & (GS - 1)) * stride]);
     mn = fminf(mn, v);
     mx = fmaxf(mx, v);
   }
@@ -45,19 +53,20 @@ __device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint1
   *zero = mn;
 #pragma unroll 8
   for (int i = 0; i < GS; ++i) {
+    const int k = (i + rot) & (GS - 1);
     uint16_t code = 0;
     if (s != 0.0f) {
-      const float t = __fdiv_rn(__fsub_rn(h2f(x[i * stride]), mn), s);
+      const float t = __fdiv_rn(__fsub_rn(h2f(x[k * stride]), mn), s);
       float r = rintf(t);
       r = fminf(fmaxf(r, 0.0f), levels);
       code = (uint16_t)r;
     }
-    codes[i * cstride] = code;
+    codes[k * cstride] = code;
   }
 }
 
-// Write the 512*bits bytes of a code block from codes[32][128] (token, channel).
-__device__ inline void pack_block(uint8_t* blk, const uint16_t (*codes)[D], int bits, bool is_v, int tid,
+// Write the 512*bits bytes of a code block from codes[32][CS] (token, channel).
+__device__ inline void pack_block(uint8_t* blk, const uint16_t (*codes)[CS], int bits, bool is_v, int tid,
                                   int nthreads) {
   const int per_word = 32 / bits;
   const int nwords = 128 * bits;
@@ -77,8 +86,10 @@ __device__ inline void pack_block(uint8_t* blk, const uint16_t (*codes)[D], int 
 }
 
 // Quantize one full 32-token group (xs: fp16 K and V [32][128], in LDS) and
-// write its record; cs is LDS scratch for the codes. 256 threads.
-__device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][D], uint8_t* rec, int kb,
+// write its record; cs is LDS scratch for the codes. 256 threads. A
+// per-token group (row j) starts at position 2j: the 16 rows a wave covers
+// then read 16 different banks.
+__device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][CS], uint8_t* rec, int kb,
                                        int vb, int k_token, int tid) {
   const RecordParts parts = record_parts(kb, vb);
   float* kmeta = (float*)(rec + parts.kmeta);
@@ -89,13 +100,13 @@ __device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*c
     } else if (!k_token) {
       const int c = tid;
       float s, z;
-      quantize32(&xs[0][0][c], D, kb, &cs[0][0][c], D, &s, &z);
+      quantize32(&xs[0][0][c], D, kb, &cs[0][0][c], CS, &s, &z);
       kmeta[meta_channel(c)] = s;
       kmeta[128 + meta_channel(c)] = z;
     } else {
       const int j = tid >> 2, n = tid & 3;
       float s, z;
-      quantize32(&xs[0][j][32 * n], 1, kb, &cs[0][j][32 * n], 1, &s, &z);
+      quantize32(&xs[0][j][32 * n], 1, kb, &cs[0][j][32 * n], 1, &s, &z, 2 * j);
       kmeta[meta_token(j, n)] = s;
       kmeta[128 + meta_token(j, n)] = z;
     }
@@ -106,7 +117,7 @@ __device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*c
     } else {
       const int j = t2 >> 2, n = t2 & 3;
       float s, z;
-      quantize32(&xs[1][j][32 * n], 1, vb, &cs[1][j][32 * n], 1, &s, &z);
+      quantize32(&xs[1][j][32 * n], 1, vb, &cs[1][j][32 * n], 1, &s, &z, 2 * j);
       vmeta[meta_token(j, n)] = s;
       vmeta[128 + meta_token(j, n)] = z;
     }

@@ -354,9 +354,14 @@ struct alignas(16) SplitSmem {
     float kmeta[kWaves][R][256];  // per wave: the key meta of up to R groups
     float vmeta[kWaves][256];     // per wave: the value meta of the current group
   };
+  struct Flush {
+    uint16_t xs[2][GS][D];   // fused append: the group's fp16 K and V
+    uint16_t cs[2][GS][CS];  // and its codes
+  };
   union {
     Loop loop;
     float o[kWaves][kMaxG][D];  // per wave: its result, for the combine
+    Flush flush;
   };
   float ml[kWaves][2][kMaxG];
   float q[kMaxG][D];  // q' of the G query rows (every wave writes the same values)
@@ -652,7 +657,7 @@ __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta,
 // packer as the append kernel), with xs/cs as LDS staging; the closing
 // barrier makes the record visible to the waves that load it.
 __device__ __forceinline__ void flush_group(uint8_t* stream, const LayerGeom& g, int m, const uint16_t* kn,
-                                            const uint16_t* vn, uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][D]) {
+                                            const uint16_t* vn, uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][CS]) {
   const int tid = threadIdx.x;
   const uint8_t* tail = stream + g.tail_offset;
   // the tail record as 1024 16-byte rows (lane l of 1 KiB row w: words 4w ..
@@ -795,9 +800,7 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
     if (L0 % GS == GS - 1) {
       const int m = L0 / GS;
       if (m >= g0 && m < g1) {
-        static_assert(sizeof(sm.o) >= 4 * GS * D * sizeof(uint16_t), "the staging fits the result buffer");
-        uint16_t(*xs)[GS][D] = reinterpret_cast<uint16_t(*)[GS][D]>(&sm.o[0][0][0]);
-        flush_group(stream, g, m, kn, vn, xs, xs + 2);
+        flush_group(stream, g, m, kn, vn, sm.flush.xs, sm.flush.cs);
       }
     }
   }
