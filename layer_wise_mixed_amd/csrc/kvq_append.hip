@@ -14,7 +14,7 @@ namespace {
 
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][GS][D];
-  __shared__ uint16_t cs[2][GS][CS];
+  __shared__ uint8_t cs[2][GS][CS];
   const LayerGeom& g = a.geo;
   const int tid = threadIdx.x;
   const int y = blockIdx.x;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 // tokens take the INT4 per-token path).
 __global__ __launch_bounds__(256) void paged_append_kernel(AppendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][GS][D];
-  __shared__ uint16_t cs[2][GS][CS];
+  __shared__ uint8_t cs[2][GS][CS];
   const LayerGeom& g = a.geo;
   const PagedGeom& pg = a.pg;
   const int tid = threadIdx.x;

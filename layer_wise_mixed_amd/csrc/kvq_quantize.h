@@ -29,16 +29,16 @@ __device__ inline void tail_put(uint8_t* rec, bool is_v, int j, int c, uint16_t 
   *(uint16_t*)(blk + word_offset(lane, e >> 1) + (e & 1) * 2) = x;
 }
 
-// LDS row stride (uint16) of the code staging: 65 words, so that a wave's
+// LDS row stride (bytes) of the code staging: 33 words, so that a wave's
 // per-token groups (rows j, column blocks 32n) and the packer's reads of 16
-// rows at once fall into different LDS banks.
-constexpr int CS = D + 2;
+// rows at once spread over the LDS banks.
+constexpr int CS = D + 4;
 
 // One group of 32 values x[i * stride]; writes codes[i * cstride], returns
 // scale/zero. The elements are visited from position rot on (mod 32): a lane
 // that starts elsewhere than its neighbours reads another LDS bank (the
 // result does not depend on the order).
-__device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint16_t* codes,
+__device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint8_t* codes,
                                   int cstride, float* scale, float* zero, int rot = 0) {
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll 8
@@ -54,34 +54,47 @@ __device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint1
 #pragma unroll 8
   for (int i = 0; i < GS; ++i) {
     const int k = (i + rot) & (GS - 1);
-    uint16_t code = 0;
+    uint8_t code = 0;
     if (s != 0.0f) {
       const float t = __fdiv_rn(__fsub_rn(h2f(x[k * stride]), mn), s);
       float r = rintf(t);
       r = fminf(fmaxf(r, 0.0f), levels);
-      code = (uint16_t)r;
+      code = (uint8_t)r;
     }
     codes[k * cstride] = code;
   }
 }
 
-// Write the 512*bits bytes of a code block from codes[32][CS] (token, channel).
-__device__ inline void pack_block(uint8_t* blk, const uint16_t (*codes)[CS], int bits, bool is_v, int tid,
-                                  int nthreads) {
-  const int per_word = 32 / bits;
-  const int nwords = 128 * bits;
+// Write the 512*BITS bytes of a code block from src[32][ROW] (token,
+// channel): the codes (BITS <= 8, uint8 rows of the staging) or the fp16
+// values themselves (BITS = 16).
+template <int BITS, bool IS_V, class T, int ROW>
+__device__ inline void pack_block(uint8_t* blk, const T (*src)[ROW], int tid, int nthreads) {
+  constexpr int per_word = 32 / BITS;
+  constexpr int nwords = 128 * BITS;
   for (int W = tid; W < nwords; W += nthreads) {
     const int lane = (W & 255) >> 2;
     const int w = (W >> 8) * 4 + (W & 3);
     uint32_t word = 0;
+#pragma unroll
     for (int p = 0; p < per_word; ++p) {
       const int e = w * per_word + p;
       int j, c;
-      if (is_v) v_inverse(lane, e, &j, &c); else k_inverse(lane, e, &j, &c);
-      const uint32_t code = codes[j][c];
-      word |= code << ((p & 1) * 16 + (p >> 1) * bits);
+      if (IS_V) v_inverse(lane, e, &j, &c); else k_inverse(lane, e, &j, &c);
+      word |= (uint32_t)src[j][c] << ((p & 1) * 16 + (p >> 1) * BITS);
     }
     *(uint32_t*)(blk + (size_t)W * 4) = word;
+  }
+}
+
+template <bool IS_V>
+__device__ inline void pack_block_bits(uint8_t* blk, int bits, const uint16_t (*xs)[D], const uint8_t (*cs)[CS],
+                                       int tid, int nthreads) {
+  switch (bits) {
+    case 2: pack_block<2, IS_V>(blk, cs, tid, nthreads); break;
+    case 4: pack_block<4, IS_V>(blk, cs, tid, nthreads); break;
+    case 8: pack_block<8, IS_V>(blk, cs, tid, nthreads); break;
+    default: pack_block<16, IS_V>(blk, xs, tid, nthreads); break;
   }
 }
 
@@ -89,14 +102,14 @@ __device__ inline void pack_block(uint8_t* blk, const uint16_t (*codes)[CS], int
 // write its record; cs is LDS scratch for the codes. 256 threads. A
 // per-token group (row j) starts at position 2j: the 16 rows a wave covers
 // then read 16 different banks.
-__device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][CS], uint8_t* rec, int kb,
+__device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint8_t (*cs)[GS][CS], uint8_t* rec, int kb,
                                        int vb, int k_token, int tid) {
   const RecordParts parts = record_parts(kb, vb);
   float* kmeta = (float*)(rec + parts.kmeta);
   float* vmeta = (float*)(rec + parts.vmeta);
   if (tid < 128) {
     if (kb == 16) {
-      for (int i = 0; i < GS; ++i) cs[0][i][tid] = xs[0][i][tid];
+      // the fp16 values are packed as they are, straight from xs
     } else if (!k_token) {
       const int c = tid;
       float s, z;
@@ -113,7 +126,7 @@ __device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*c
   } else {
     const int t2 = tid - 128;
     if (vb == 16) {
-      for (int i = 0; i < GS; ++i) cs[1][i][t2] = xs[1][i][t2];
+      // packed from xs
     } else {
       const int j = t2 >> 2, n = t2 & 3;
       float s, z;
@@ -123,8 +136,8 @@ __device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint16_t (*c
     }
   }
   __syncthreads();
-  pack_block(rec, cs[0], kb, false, tid, blockDim.x);
-  pack_block(rec + parts.vcode, cs[1], vb, true, tid, blockDim.x);
+  pack_block_bits<false>(rec, kb, xs[0], cs[0], tid, blockDim.x);
+  pack_block_bits<true>(rec + parts.vcode, vb, xs[1], cs[1], tid, blockDim.x);
 }
 
 }  // namespace

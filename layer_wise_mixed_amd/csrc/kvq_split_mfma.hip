@@ -356,7 +356,7 @@ struct alignas(16) SplitSmem {
   };
   struct Flush {
     uint16_t xs[2][GS][D];   // fused append: the group's fp16 K and V
-    uint16_t cs[2][GS][CS];  // and its codes
+    uint8_t cs[2][GS][CS];   // and its codes
   };
   union {
     Loop loop;
@@ -657,7 +657,7 @@ __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta,
 // packer as the append kernel), with xs/cs as LDS staging; the closing
 // barrier makes the record visible to the waves that load it.
 __device__ __forceinline__ void flush_group(uint8_t* stream, const LayerGeom& g, int m, const uint16_t* kn,
-                                            const uint16_t* vn, uint16_t (*xs)[GS][D], uint16_t (*cs)[GS][CS]) {
+                                            const uint16_t* vn, uint16_t (*xs)[GS][D], uint8_t (*cs)[GS][CS]) {
   const int tid = threadIdx.x;
   const uint8_t* tail = stream + g.tail_offset;
   // the tail record as 1024 16-byte rows (lane l of 1 KiB row w: words 4w ..
