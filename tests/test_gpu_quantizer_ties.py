@@ -3,7 +3,10 @@ rounding ties of (x - zero) / scale, where a quotient that is off by one ulp, or
 that is not half-to-even, changes a code: every 32-token channel group and every 32-channel
 token group holds 0 and levels * 2^-k, so scale = 2^-k exactly, and the other values are
 (m + 1/2) 2^-k or their fp16 neighbours. Through the prefill append, the decode append (one
-token at a time, so groups flush from the tail) and the fused append-and-decode pass."""
+token at a time, so groups flush from the tail) and the fused append-and-decode pass. Groups
+that hold their own midpoint put (mid - min) / scale within a rounding or two of
+(2^b - 1) / 2, where any quotient other than the correctly rounded one can round the other
+way."""
 import math
 
 import numpy as np
@@ -28,6 +31,27 @@ def _tie_values(bits, L, k, seed):
     j, c = np.meshgrid(np.arange(L), np.arange(128), indexing="ij")
     x = np.where((j + c) % 7 == 0, np.float16(0.0), x)
     x = np.where((j + c) % 7 == 1, np.float16(levels * step), x)
+    return x.astype(np.float16)
+
+
+def _midpoint_values(L, seed, per_token):
+    """fp16 [L, 128] whose every group (32 tokens of a channel, or 32 channels of a token when
+    per_token) holds its min, its max and their midpoint, so that (mid - min) / scale lies
+    within a rounding of the half-integer (2^b - 1) / 2 for every width b."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((L, 128), np.float32)
+    for g0 in range(0, L if not per_token else 128, 32):
+        n = L if per_token else 128
+        for k in range(n):
+            mn = np.float32(rng.uniform(-20, 20))
+            mx = np.float32(np.float16(mn + np.float32(rng.uniform(1e-2, 50))))
+            mn = np.float32(np.float16(mn))
+            vals = rng.uniform(mn, mx, 32).astype(np.float32)
+            vals[rng.permutation(32)[:3]] = [mn, mx, np.float16(mn + (mx - mn) / 2)]
+            if per_token:
+                x[k, g0:g0 + 32] = vals
+            else:
+                x[g0:g0 + 32, k] = vals[:min(32, L - g0)]
     return x.astype(np.float16)
 
 
@@ -56,6 +80,20 @@ def test_prefill_append_ties(gpu, oq):
     plan = gpu.plan_layers(gpu.make_shape(hkv * 2, hkv, 1, max_tokens=L), CFGS)
     cache = torch.zeros(plan.total_bytes, dtype=torch.uint8, device="cuda")
     ks, vs = _streams(L, hkv, 1)
+    z = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for l in range(len(CFGS)):
+        gpu.quantize_append(plan, l, cache, torch.from_numpy(ks[l][None]).cuda(), torch.from_numpy(vs[l][None]).cuda(),
+                            z)
+    torch.cuda.synchronize()
+    _check(gpu, oq, plan, cache, ks, vs, L, hkv)
+
+
+def test_prefill_append_midpoints(gpu, oq):
+    L, hkv = 96, 2
+    plan = gpu.plan_layers(gpu.make_shape(hkv * 2, hkv, 1, max_tokens=L), CFGS)
+    cache = torch.zeros(plan.total_bytes, dtype=torch.uint8, device="cuda")
+    ks = [np.stack([_midpoint_values(L, 100 * l + h, CFGS[l][2] == 1) for h in range(hkv)]) for l in range(len(CFGS))]
+    vs = [np.stack([_midpoint_values(L, 100 * l + h + 50, True) for h in range(hkv)]) for l in range(len(CFGS))]
     z = torch.zeros(1, dtype=torch.int32, device="cuda")
     for l in range(len(CFGS)):
         gpu.quantize_append(plan, l, cache, torch.from_numpy(ks[l][None]).cuda(), torch.from_numpy(vs[l][None]).cuda(),
