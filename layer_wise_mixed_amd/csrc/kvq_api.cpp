@@ -148,7 +148,7 @@ int64_t capacity_tokens(const kvq_plan* plan, const kvq_pages* pages) {
   return is_paged(plan) ? (int64_t)pages->max_pages_per_req * kvq::PAGE_TOKENS : plan->shape.max_tokens;
 }
 
-// A paged split walks at most 256 groups (64 per wave).
+// A paged split walks at most 256 complete groups (64 per wave).
 constexpr int64_t kPagedMaxGroupsPerSplit = 256;
 
 int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
@@ -156,15 +156,17 @@ int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
   const int64_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
   if (nvg <= 0 || streams <= 0) return 1;
   if (is_paged(plan)) {
-    // one kind per split: ceil(nvg / gps) + 1 splits cover a request's INT2
-    // groups and its INT4 page pairs together
-    int64_t s = (512 + streams - 1) / streams;
-    const int64_t s_min = (nvg + kPagedMaxGroupsPerSplit - 1) / kPagedMaxGroupsPerSplit;
+    // one kind per split, so ceil(nvg / gps) + 1 splits cover a request's
+    // INT2 groups and its INT4 page pairs together (gps = ceil(nvg / (splits
+    // - 1)) <= 256). Aim for ~1024 workgroups, two full rounds at two per CU:
+    // INT4 splits carry 1.5x the bytes of INT2 ones, and a second round lets
+    // the CUs that drew INT2 splits take more work (one round of 512, or a
+    // round and a half, measured 15-25% slower).
+    int64_t s = (1024 + streams - 1) / streams;
+    const int64_t s_min = (nvg + kPagedMaxGroupsPerSplit - 1) / kPagedMaxGroupsPerSplit + 1;
     if (s < s_min) s = s_min;
-    if (s > nvg) s = nvg;
-    const int64_t gps = (nvg + s - 1) / s;
-    const int64_t n = (nvg + gps - 1) / gps + 1;
-    return (int32_t)(n > 1024 ? 1024 : n);
+    if (s > nvg + 1) s = nvg + 1;
+    return (int32_t)(s > 1024 ? 1024 : s);
   }
   // 4-wave workgroups: aim for ~512 of them (2 per CU on 256 CUs), but keep
   // at least 8 groups (2 per wave) in each split

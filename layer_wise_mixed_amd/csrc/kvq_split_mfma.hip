@@ -912,15 +912,21 @@ __global__ __launch_bounds__(256, 2) void paged_split_kernel(DecodeArgs a) {
   const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int n2 = max(a.pg.int2_len[r], 0), n4 = max(a.pg.int4_len[r], 0);
   const int gps = a.groups_per_split;
-  const int n2g = n2 / GS, n4g = (n4 + GS - 1) / GS;
+  const int n2g = n2 / GS, n4g = (n4 + GS - 1) / GS, full4 = n4 / GS;
   const int s2 = (n2g + gps - 1) / gps;  // splits of the INT2 part
+  // splits of the INT4 part: gps complete page pairs each; a last, partly
+  // filled pair joins the last of them (a split of its own without complete
+  // pairs); splits past these stay empty
+  const int s4 = full4 > 0 ? (full4 + gps - 1) / gps : (n4g > 0 ? 1 : 0);
   const int32_t* table = a.pg.table + (size_t)r * a.pg.max_pages;
   if (split < s2) {
     const int g0 = split * gps;
     paged_int2_split<NS>(a, sm, r, h, split, g0, min(g0 + gps, n2g), table);
   } else {
-    const int g0 = (split - s2) * gps;
-    paged_int4_split<NS>(a, sm, r, h, split, g0, min(g0 + gps, n4g), n4, table + n2 / PAGE_TOKENS);
+    const int i = split - s2;
+    const int g0 = i < s4 ? i * gps : n4g;
+    const int g1 = i < s4 - 1 ? g0 + gps : n4g;
+    paged_int4_split<NS>(a, sm, r, h, split, g0, g1, n4, table + n2 / PAGE_TOKENS);
   }
 }
 
