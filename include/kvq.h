@@ -305,8 +305,10 @@ int kvq_dequantize(const kvq_plan *plan, int32_t layer, const void *cache,
                    const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float *k_out,
                    float *v_out, const kvq_pages *pages, kvq_stream_t stream);
 
-/* Alignment: the kernels read the cache, k_new, v_new and q in 16-byte
- * pieces; a call given one of them not 16-byte aligned returns INVALID_ARG. */
+/* Alignment: the kernels read the cache, k_new, v_new, q and the split
+ * partials in the workspace, and write out, in 16-byte pieces (an fp16 out
+ * in 8-byte pieces); a call given one of them not 16-byte aligned returns
+ * INVALID_ARG. */
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *kvq_last_error(void);

@@ -179,8 +179,9 @@ int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
 }
 
 // Prefix attention: the row blocks already give batch * Hkv * blocks
-// workgroups; split the prefix only while that is under ~512, keeping at
-// least 8 groups in each split.
+// workgroups (8 waves, one per CU); split the prefix only while that is
+// under one round of 256, keeping at least 8 groups in each split (a second
+// round, or more splits, measured slower once the merge is counted).
 int64_t prefix_blocks(const kvq_plan* plan, int32_t chunk) {
   const int64_t rows = (int64_t)chunk * (plan->shape.num_q_heads / plan->shape.num_kv_heads);
   return (rows + kvq::prefix_rows_per_block() - 1) / kvq::prefix_rows_per_block();
@@ -190,7 +191,7 @@ int32_t prefix_splits(const kvq_plan* plan, int32_t batch, int32_t chunk, int32_
   const int64_t wgs = (int64_t)batch * plan->shape.num_kv_heads * prefix_blocks(plan, chunk);
   const int64_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
   if (nvg <= 0 || wgs <= 0) return 1;
-  int64_t s = (512 + wgs - 1) / wgs;
+  int64_t s = (256 + wgs - 1) / wgs;
   const int64_t max_s = nvg / 8 > 1 ? nvg / 8 : 1;
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
@@ -328,7 +329,8 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   int st = check_plan_layer(plan, layer);
   if (st) return st;
   if (!cache || !q || !out) return fail(KVQ_ERR_INVALID_ARG, "null cache, q or out");
-  if (!aligned16(cache) || !aligned16(q)) return fail(KVQ_ERR_INVALID_ARG, "cache and q must be 16-byte aligned");
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || !aligned16(workspace))
+    return fail(KVQ_ERR_INVALID_ARG, "cache, q, out and workspace must be 16-byte aligned");
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
   if (out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_F32)
@@ -401,8 +403,9 @@ int kvq_append_decode_attention(const kvq_plan* plan, int32_t layer, void* cache
     return fail(KVQ_ERR_UNSUPPORTED, "a paged pool appends and decodes with kvq_quantize_append and "
                                      "kvq_decode_attention");
   if (!cache || !k_new || !v_new || !q || !out) return fail(KVQ_ERR_INVALID_ARG, "null cache, input or output");
-  if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(q))
-    return fail(KVQ_ERR_INVALID_ARG, "cache, k_new, v_new and q must be 16-byte aligned");
+  if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out) ||
+      !aligned16(workspace))
+    return fail(KVQ_ERR_INVALID_ARG, "cache, k_new, v_new, q, out and workspace must be 16-byte aligned");
   if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);

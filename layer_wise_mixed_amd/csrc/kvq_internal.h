@@ -198,7 +198,7 @@ struct MergeArgs {
   const float* part_o;
   const float* part_lse;
   int splits;
-  int rows;  // batch * Hq
+  int rows;  // output rows (batch * Hq; prefix attention: batch * chunk * Hq)
   void* out;
   int out_f32;
   float* lse_out;

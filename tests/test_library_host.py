@@ -274,8 +274,8 @@ def test_prefix_workspace_and_auto_splits():
     # a workgroup takes 256 rows (64 tokens x 4 heads): 4 requests x 8 KV heads x 16 blocks
     # of a 1024-token chunk fill the chip with one split
     assert kvq.prefix_workspace_bytes(plan, 4, 1024, 4096) == 0
-    # 2 x 8 x 4 blocks of a 256-token chunk: 64 workgroups, 8 splits
-    assert kvq.prefix_workspace_bytes(plan, 2, 256, 4096) == 2 * 256 * 32 * 8 * 129 * 4
+    # 2 x 8 x 4 blocks of a 256-token chunk: 64 workgroups, 4 splits make one round of 256
+    assert kvq.prefix_workspace_bytes(plan, 2, 256, 4096) == 2 * 256 * 32 * 4 * 129 * 4
     # one 4-token chunk: 8 workgroups, so the prefix is split, into 16 splits of 8 groups (a
     # split keeps at least 8 of the 128)
     assert kvq.prefix_workspace_bytes(plan, 1, 4, 4096) == 1 * 4 * 32 * 16 * 129 * 4
