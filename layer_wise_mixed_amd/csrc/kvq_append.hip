@@ -12,12 +12,16 @@
 namespace kvq {
 namespace {
 
+// One workgroup per (x, stream); it completes the x-th of gridDim.x runs of
+// consecutive groups of this call, and while one group is quantized the fp16
+// rows of its next whole-new group are already loading (in registers), so
+// that the stream of loads does not stop for the arithmetic.
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][GS][D];
   __shared__ uint8_t cs[2][GS][CS];
   const LayerGeom& g = a.geo;
   const int tid = threadIdx.x;
-  const int y = blockIdx.x;
   const int sigma = blockIdx.y;
   const int r = sigma / g.hkv;
   const int L0 = a.seq_lens[r];
@@ -30,27 +34,32 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const uint16_t* kn = a.k_new + (size_t)sigma * a.n_new * D;
   const uint16_t* vn = a.v_new + (size_t)sigma * a.n_new * D;
 
-  if (y < F) {
+  // a whole-new group's 32 contiguous rows of k_new and of v_new, 8 KiB each,
+  // two 16-byte pieces a thread and tensor
+  constexpr int kPer = GS * D / 8 / 256;
+  u4_t ka[kPer], va[kPer];
+  auto fetch = [&](int y) {
+    const u4_t* ks = (const u4_t*)(kn + (size_t)(GS * (m0 + y) - L0) * D);
+    const u4_t* vs = (const u4_t*)(vn + (size_t)(GS * (m0 + y) - L0) * D);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      ka[q] = ks[tid + 256 * q];
+      va[q] = vs[tid + 256 * q];
+    }
+  };
+  auto whole_new = [&](int y) { return GS * (m0 + y) >= L0; };
+
+  const int run = (F + gridDim.x - 1) / gridDim.x;
+  const int yend = min(F, (blockIdx.x + 1) * run);
+  int y = blockIdx.x * run;
+  if (y < yend && whole_new(y)) fetch(y);
+  for (; y < yend; ++y) {
     const int m = m0 + y;
-    if (GS * m >= L0) {
-      // the whole group is new: 32 contiguous rows of k_new and of v_new, 8 KiB
-      // each, copied in 16-byte pieces, all loads issued before any store
-      typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
-      const u4_t* ks = (const u4_t*)(kn + (size_t)(GS * m - L0) * D);
-      const u4_t* vs = (const u4_t*)(vn + (size_t)(GS * m - L0) * D);
-      u4_t* kd = (u4_t*)&xs[0][0][0];
-      u4_t* vd = (u4_t*)&xs[1][0][0];
-      constexpr int kPieces = GS * D / 8;  // 512 per tensor
-      u4_t a[kPieces / 256], b[kPieces / 256];
+    if (whole_new(y)) {
 #pragma unroll
-      for (int q = 0; q < kPieces / 256; ++q) {
-        a[q] = ks[tid + 256 * q];
-        b[q] = vs[tid + 256 * q];
-      }
-#pragma unroll
-      for (int q = 0; q < kPieces / 256; ++q) {
-        kd[tid + 256 * q] = a[q];
-        vd[tid + 256 * q] = b[q];
+      for (int q = 0; q < kPer; ++q) {
+        ((u4_t*)&xs[0][0][0])[tid + 256 * q] = ka[q];
+        ((u4_t*)&xs[1][0][0])[tid + 256 * q] = va[q];
       }
     } else {
       for (int idx = tid; idx < GS * D; idx += blockDim.x) {
@@ -69,10 +78,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       }
     }
     __syncthreads();
+    if (y + 1 < yend && whole_new(y + 1)) fetch(y + 1);  // in flight during the quantization
     quantize_record(xs, cs, stream + (size_t)m * g.record_bytes, g.kb, g.vb, g.k_token, tid);
+    __syncthreads();  // the next group rewrites xs and cs
   }
-  if (y == 0) {
-    __syncthreads();  // the flush above has read the old tail slots
+  if (blockIdx.x == 0) {  // after its flush (if any) has read the old tail slots
     const int tstart = max(L0, GS * (L1 / GS));
     const int nt = L1 - tstart;
     for (int idx = tid; idx < nt * D; idx += blockDim.x) {
@@ -279,7 +289,17 @@ hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s) 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev) {
   const int y = a.n_new > 0 ? (a.n_new + GS - 1) / GS : 0;
   if (y == 0 || batch == 0) return hipSuccess;
-  return launch_timed(append_kernel, dim3(y, batch * a.geo.hkv), dim3(256), s, ev, a);
+  // long appends (prefill): two rounds of workgroups (6 fit a CU by their
+  // LDS, 256 CUs), each looping over a run of its stream's groups (one round
+  // measured up to 7% slower, a workgroup per group up to 40% slower); short
+  // ones: a workgroup per group
+  const int streams = batch * a.geo.hkv;
+  int x = y;
+  if (y > 8) {
+    x = (3072 + streams - 1) / streams;
+    if (x > y) x = y;
+  }
+  return launch_timed(append_kernel, dim3(x, streams), dim3(256), s, ev, a);
 }
 
 hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s) {
