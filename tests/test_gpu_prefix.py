@@ -143,3 +143,19 @@ def test_large_chunk_sampled(gpu, oq):
                     rel = np.linalg.norm(got - o) / np.linalg.norm(o)
                     assert rel <= 1e-3 and np.abs(got - o).max() <= 2e-3, f"l{l} r{r} h{h} i{i}: rel {rel:.3g}"
                     assert np.abs(lse[r, i, h * G:(h + 1) * G] - ls).max() <= 1e-4
+
+
+@pytest.mark.parametrize("hq,hkv,chunk,splits", [(14, 2, 100, 0), (6, 2, 200, 3), (28, 4, 40, 1)])
+def test_row_blocks_split_a_token(gpu, oq, hq, hkv, chunk, splits):
+    # a workgroup takes 256 rows; with G = 7 or 3 a chunk token's query heads straddle two
+    # row blocks, and every row must still land in its own place
+    c = Case(gpu, oq, hq=hq, hkv=hkv, batch=3, cap=160, cfgs=[(4, 2), (8, 4, 1), (2, 8)], lens=[160, 77, 5], seed=8)
+    for l in range(len(c.cfgs)):
+        q = chunk_queries(c.seed, l, c.batch, hq, 160, chunk)
+        out, lse = run_prefix(gpu, c, l, q, splits)
+        ref, ref_lse = oracle_prefix(oq, c, l, q)
+        try:
+            check_attention(out.reshape(c.batch, -1, 128), lse.reshape(c.batch, -1), ref.reshape(c.batch, -1, 128),
+                            ref_lse.reshape(c.batch, -1), c.lens, hq)
+        except AssertionError as e:
+            raise AssertionError(f"layer {l} {c.cfgs[l]}: {e}") from None
