@@ -253,12 +253,13 @@ class PagedWorkload:
 
     PAGE = 16
 
-    def __init__(self, name, seed=0, device="cuda", num_splits=0, layers=None):
+    def __init__(self, name, seed=0, device="cuda", num_splits=0, layers=None, fused=True):
         import torch
 
         import layer_wise_mixed_amd as kvq
 
         self.name, self.seed, self.kvq = name, seed, kvq
+        self.fused = fused
         w = self.w = WORKLOADS[name]
         self.layer_ids = list(range(w["layers"])) if layers is None else list(layers)
         self.L, self.B, self.Hq, self.Hkv = len(self.layer_ids), w["batch"], w["hq"], w["hkv"]
@@ -341,11 +342,19 @@ class PagedWorkload:
         self.n4_after.add_(1)
 
     def step(self, i):
+        """One decode step: per layer, the new INT4 token appended inside the paged split pass
+        (plus the merge), or with fused=False the append kernel, then the decode."""
         kvq = self.kvq
         for l in range(self.L):
-            kvq.quantize_append(self.plan, l, self.cache, self.k_dec[l][i], self.v_dec[l][i], None, self.pages_append)
-            kvq.decode_attention(self.plan, l, self.cache, self.q[l][i], None, self.max_len, self.scale, self.out,
-                                 None, self.ws, self.splits, pages=self.pages_decode)
+            if self.fused:
+                kvq.append_decode_attention(self.plan, l, self.cache, self.k_dec[l][i], self.v_dec[l][i],
+                                            self.q[l][i], None, self.max_len, self.scale, self.out, None, self.ws,
+                                            self.splits, pages=self.pages_append)
+            else:
+                kvq.quantize_append(self.plan, l, self.cache, self.k_dec[l][i], self.v_dec[l][i], None,
+                                    self.pages_append)
+                kvq.decode_attention(self.plan, l, self.cache, self.q[l][i], None, self.max_len, self.scale,
+                                     self.out, None, self.ws, self.splits, pages=self.pages_decode)
         self.n4_before.add_(1)
         self.n4_after.add_(1)
 
@@ -491,7 +500,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--unfused", action="store_true",
-                    help="contiguous workloads: append with its own launch instead of inside the split pass")
+                    help="append with its own launch instead of inside the split pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
@@ -524,8 +533,7 @@ def main():
     kvq.load()
     t_setup = time.perf_counter()
     cls = PagedWorkload if WORKLOADS[args.workload].get("paged") else Workload
-    wl = cls(args.workload, seed=args.seed, num_splits=args.splits, **({} if cls is PagedWorkload else
-                                                                       {"fused": not args.unfused}))
+    wl = cls(args.workload, seed=args.seed, num_splits=args.splits, fused=not args.unfused)
     fused = getattr(wl, "fused", False)
     K = args.steps if args.steps is not None else wl.C
     W = args.warmup if args.warmup is not None else min(wl.C, 16)

@@ -228,30 +228,33 @@ int kvq_decode_attention(const kvq_plan *plan, int32_t layer, const void *cache,
  * kvq_append_decode_attention -- one decode step of one layer with its token
  * append fused in: the same result, in the cache and in out/lse_out, as
  * kvq_quantize_append with n_new = 1 followed by kvq_decode_attention with
- * every seq_lens[r] one larger, in one split pass (plus the merge pass when
+ * every length one larger, in one split pass (plus the merge pass when
  * there are several splits). The workgroup whose split holds the new
- * token's place appends it: into the fp16 tail record, or, when it completes
- * a 32-token group, by quantizing and packing that group before any wave
- * reads it (TriAxialKV page, "Facts", quantizer bullet, as in
- * kvq_quantize_append). This saves the append launch of every decode step.
+ * token's place appends it before any wave reads that place: into the fp16
+ * tail record, or, when it completes a 32-token group, by quantizing and
+ * packing that group (TriAxialKV page, "Facts", quantizer bullet, as in
+ * kvq_quantize_append); in a paged pool, into the request's INT4 page as a
+ * per-token INT4 token (TriAxialKV page, "Facts": decoded tokens take the
+ * INT4 per-token path). This saves the append launch of every decode step.
  *   k_new, v_new: device fp16 [batch][Hkv][1][128], the new token;
  *   seq_lens: device [batch] tokens per request BEFORE the append (the
  *     caller advances them afterwards, as with kvq_quantize_append); a
  *     stream at max_tokens is left unchanged and attended as it is;
- *   max_seq_len: host bound of seq_lens[r] + 1 (at least 1);
+ *   pages: NULL for a contiguous plan; for a paged plan, int4_len counts
+ *     the INT4 tokens BEFORE the append (the caller advances it) and
+ *     int2_add must be NULL; seq_lens is then ignored;
+ *   max_seq_len: host bound of the lengths + 1 (at least 1);
  *   q, softmax_scale, out, out_dtype, lse_out, workspace, num_splits: as in
  *     kvq_decode_attention (workspace sized by kvq_decode_workspace_bytes
- *     with the same max_seq_len).
- * Contiguous plans only: a paged pool uses the two calls.
- *   Errors: INVALID_ARG, UNSUPPORTED (paged plan), CAPACITY (max_seq_len >
- *   max_tokens), WORKSPACE, HIP.
+ *     with the same max_seq_len; a paged pool has its split limits).
+ *   Errors: INVALID_ARG, CAPACITY (max_seq_len > capacity), WORKSPACE, HIP.
  */
 int kvq_append_decode_attention(const kvq_plan *plan, int32_t layer, void *cache,
                                 const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q,
                                 const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
                                 float softmax_scale, void *out, int32_t out_dtype, float *lse_out,
                                 void *workspace, size_t workspace_bytes, int32_t num_splits,
-                                kvq_stream_t stream);
+                                const kvq_pages *pages, kvq_stream_t stream);
 
 /* Workspace bytes kvq_prefix_attention needs: 0 when it uses one split, else
  * batch * chunk * Hq * splits * (128 + 1) fp32. num_splits = 0 means the

@@ -100,7 +100,7 @@ def load():
                                        ctypes.c_size_t, i32, ctypes.POINTER(Pages), P]
     L.kvq_decode_attention.restype = ctypes.c_int
     L.kvq_append_decode_attention.argtypes = [ctypes.POINTER(Plan), i32, P, P, P, P, P, i32, i32, ctypes.c_float,
-                                              P, i32, P, P, ctypes.c_size_t, i32, P]
+                                              P, i32, P, P, ctypes.c_size_t, i32, ctypes.POINTER(Pages), P]
     L.kvq_append_decode_attention.restype = ctypes.c_int
     L.kvq_prefix_workspace_bytes.argtypes = [ctypes.POINTER(Plan), i32, i32, i32, i32]
     L.kvq_prefix_workspace_bytes.restype = ctypes.c_size_t
@@ -210,10 +210,12 @@ def decode_attention(plan: Plan, layer: int, cache, q, seq_lens, max_seq_len: in
 
 
 def append_decode_attention(plan: Plan, layer: int, cache, k_new, v_new, q, seq_lens, max_seq_len: int,
-                            softmax_scale: float, out, lse=None, workspace=None, num_splits: int = 0, stream=None):
+                            softmax_scale: float, out, lse=None, workspace=None, num_splits: int = 0,
+                            pages: Pages | None = None, stream=None):
     """One token appended per request and the decode step over the cache with it, in one pass.
-    k_new, v_new: fp16 [batch, Hkv, 1, 128]; seq_lens: lengths before the append (not advanced here);
-    max_seq_len: bound of seq_lens + 1; q, out, lse, workspace, num_splits: as in decode_attention."""
+    k_new, v_new: fp16 [batch, Hkv, 1, 128]; seq_lens: lengths before the append (not advanced here;
+    ignored with pages, whose int4_len holds the INT4 lengths before the append); max_seq_len: bound
+    of the lengths + 1; q, out, lse, workspace, num_splits: as in decode_attention."""
     import torch
 
     assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16
@@ -222,12 +224,14 @@ def append_decode_attention(plan: Plan, layer: int, cache, k_new, v_new, q, seq_
     assert out.is_contiguous() and out.dtype in (torch.float16, torch.float32)
     batch = q.shape[0]
     assert k_new.shape[0] == batch
-    _dev_i32(seq_lens, batch, "seq_lens")
+    if pages is None:
+        _dev_i32(seq_lens, batch, "seq_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kvq_append_decode_attention(ctypes.byref(plan), layer, _ptr(cache), _ptr(k_new), _ptr(v_new),
                                               _ptr(q), _ptr(seq_lens), batch, max_seq_len, float(softmax_scale),
                                               _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
-                                              _ptr(lse), _ptr(workspace), ws_bytes, num_splits, _stream(stream)))
+                                              _ptr(lse), _ptr(workspace), ws_bytes, num_splits,
+                                              None if pages is None else ctypes.byref(pages), _stream(stream)))
 
 
 def prefix_workspace_bytes(plan: Plan, batch: int, chunk: int, max_seq_len: int, num_splits: int = 0) -> int:

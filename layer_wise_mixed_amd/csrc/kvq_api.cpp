@@ -178,6 +178,27 @@ int32_t auto_splits(const kvq_plan* plan, int32_t batch, int32_t max_seq_len) {
   return (int32_t)s;
 }
 
+// Groups per split for `splits` splits of max_seq_len tokens. A paged pool
+// gives a request's INT2 and INT4 parts splits of their own, so it needs one
+// split more and at most kPagedMaxGroupsPerSplit groups a split.
+int split_groups(const kvq_pages* pages, int32_t splits, int32_t max_seq_len, int32_t* gps) {
+  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
+  if (!pages) {
+    *gps = nvg > 0 ? (nvg + splits - 1) / splits : 0;
+    return KVQ_OK;
+  }
+  if (nvg == 0) {
+    *gps = 1;  // no tokens anywhere; the kernels divide by gps
+    return KVQ_OK;
+  }
+  if (splits < 2) return fail(KVQ_ERR_INVALID_ARG, "a paged decode needs at least 2 splits");
+  *gps = (nvg + splits - 2) / (splits - 1);
+  if (*gps > kPagedMaxGroupsPerSplit)
+    return fail(KVQ_ERR_INVALID_ARG, "num_splits %d too small: a paged split walks at most %lld groups", splits,
+                (long long)kPagedMaxGroupsPerSplit);
+  return KVQ_OK;
+}
+
 // Prefix attention: the row blocks already give batch * Hkv * blocks
 // workgroups (8 waves, one per CU); split the prefix only while that is
 // under one round of 256, keeping at least 8 groups in each split (a second
@@ -345,17 +366,8 @@ int kvq_decode_attention(const kvq_plan* plan, int32_t layer, const void* cache,
                 (long long)capacity_tokens(plan, pages));
   if (batch == 0) return ok();
   const int32_t splits = num_splits ? num_splits : auto_splits(plan, batch, max_seq_len);
-  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
-  int32_t gps = nvg > 0 ? (nvg + splits - 1) / splits : 0;
-  if (pages && nvg == 0) gps = 1;  // no tokens anywhere; the kernels divide by gps
-  if (pages && nvg > 0) {
-    // a request's INT2 and INT4 parts start splits of their own: one split more
-    if (splits < 2) return fail(KVQ_ERR_INVALID_ARG, "a paged decode needs at least 2 splits");
-    gps = (nvg + splits - 2) / (splits - 1);
-    if (gps > kPagedMaxGroupsPerSplit)
-      return fail(KVQ_ERR_INVALID_ARG, "num_splits %d too small: a paged split walks at most %lld groups", splits,
-                  (long long)kPagedMaxGroupsPerSplit);
-  }
+  int32_t gps = 0;
+  if ((st = split_groups(pages, splits, max_seq_len, &gps))) return st;
   const size_t need = (size_t)batch * plan->shape.num_q_heads * splits * (kvq::D + 1) * sizeof(float);
   if (!workspace || workspace_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
@@ -396,17 +408,17 @@ int kvq_append_decode_attention(const kvq_plan* plan, int32_t layer, void* cache
                                 const uint16_t* v_new, const uint16_t* q, const int32_t* seq_lens, int32_t batch,
                                 int32_t max_seq_len, float softmax_scale, void* out, int32_t out_dtype,
                                 float* lse_out, void* workspace, size_t workspace_bytes, int32_t num_splits,
-                                kvq_stream_t stream) {
+                                const kvq_pages* pages, kvq_stream_t stream) {
   int st = check_plan_layer(plan, layer);
   if (st) return st;
-  if (is_paged(plan))
-    return fail(KVQ_ERR_UNSUPPORTED, "a paged pool appends and decodes with kvq_quantize_append and "
-                                     "kvq_decode_attention");
   if (!cache || !k_new || !v_new || !q || !out) return fail(KVQ_ERR_INVALID_ARG, "null cache, input or output");
   if (!aligned16(cache) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out) ||
       !aligned16(workspace))
     return fail(KVQ_ERR_INVALID_ARG, "cache, k_new, v_new, q, out and workspace must be 16-byte aligned");
-  if (!seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if ((st = check_pages(plan, pages))) return st;
+  if (!pages && !seq_lens) return fail(KVQ_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (pages && pages->int2_add)
+    return fail(KVQ_ERR_INVALID_ARG, "a fused paged step appends one INT4 token a request: int2_add must be NULL");
   if (batch < 0 || batch > plan->shape.max_batch)
     return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
   if (out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_F32)
@@ -414,19 +426,19 @@ int kvq_append_decode_attention(const kvq_plan* plan, int32_t layer, void* cache
   if (num_splits < 0 || num_splits > 1024) return fail(KVQ_ERR_INVALID_ARG, "num_splits %d", num_splits);
   if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (max_seq_len < 1) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 1 (it counts the appended token)", max_seq_len);
-  if (max_seq_len > capacity_tokens(plan, nullptr))
+  if (max_seq_len > capacity_tokens(plan, pages))
     return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > %lld tokens of capacity", max_seq_len,
-                (long long)capacity_tokens(plan, nullptr));
+                (long long)capacity_tokens(plan, pages));
   if (batch == 0) return ok();
   const int32_t splits = num_splits ? num_splits : auto_splits(plan, batch, max_seq_len);
-  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
-  const int32_t gps = (nvg + splits - 1) / splits;
+  int32_t gps = 0;
+  if ((st = split_groups(pages, splits, max_seq_len, &gps))) return st;
   const size_t need = (size_t)batch * plan->shape.num_q_heads * splits * (kvq::D + 1) * sizeof(float);
   if (!workspace || workspace_bytes < need)
     return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   kvq::DecodeArgs a;
   a.geo = geom(plan, layer, cache);
-  a.pg = paged_geom(plan, layer, nullptr);
+  a.pg = paged_geom(plan, layer, pages);
   a.q = q;
   a.seq_lens = seq_lens;
   a.splits = splits;
@@ -442,7 +454,8 @@ int kvq_append_decode_attention(const kvq_plan* plan, int32_t layer, void* cache
   hipStream_t s = (hipStream_t)stream;
   kvq::EventPair ev;
   bool timed = timer_slot(1, &ev);
-  hipError_t e = kvq::launch_decode_split_mfma(a, batch, s, timed ? &ev : nullptr);
+  hipError_t e = pages ? kvq::launch_decode_paged(a, batch, s, timed ? &ev : nullptr)
+                       : kvq::launch_decode_split_mfma(a, batch, s, timed ? &ev : nullptr);
   if (e != hipSuccess) return hip_status(e, "fused append and split launch");
   if (splits == 1) return ok();
   kvq::MergeArgs m;

@@ -140,5 +140,58 @@ __device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint8_t (*cs
   pack_block_bits<true>(rec + parts.vcode, vb, xs[1], cs[1], tid, blockDim.x);
 }
 
+// Write slots p_lo .. p_hi - 1 of one KV head's share of an INT4 page (keys
+// and values per-token at 4 bits, TriAxialKV page, "Facts": INT4 per-token
+// path): their fp16 rows are in xs[tensor][slot] (LDS, visible to every
+// thread); cs is LDS scratch for the codes. 256 threads, all of them must
+// call. Value words hold four slots: the slots outside the range keep their
+// bits.
+__device__ inline void page_append_int4(uint8_t* page, const uint16_t (*xs)[GS][D], uint8_t (*cs)[GS][CS], int p_lo,
+                                        int p_hi, int tid) {
+  if (tid < 128) {  // per-token quantization: (tensor, slot, channel group)
+    const int tensor = tid >> 6, p = (tid >> 2) & 15, n = tid & 3;
+    if (p >= p_lo && p < p_hi) {
+      float s, z;
+      quantize32(&xs[tensor][p][32 * n], 1, 4, &cs[tensor][p][32 * n], 1, &s, &z, 2 * p);
+      float* meta = (float*)(page + (tensor ? INT4_VMETA : INT4_KMETA));
+      meta[16 * n + p] = s;
+      meta[64 + 16 * n + p] = z;
+    }
+  }
+  __syncthreads();
+  {  // key words: the 8 codes of a word belong to one slot
+    const int p = tid >> 4, a4 = (tid >> 2) & 3, w = tid & 3;
+    if (p >= p_lo && p < p_hi) {
+      uint32_t word = 0;
+      for (int pos = 0; pos < 8; ++pos) {
+        int sh;
+        const int c = 32 * w + 8 * a4 + pos;
+        (void)page_k_offset(p, c, &sh);
+        word |= (uint32_t)cs[0][p][c] << sh;
+      }
+      int sh0;
+      *(uint32_t*)(page + page_k_offset(p, 32 * w + 8 * a4, &sh0)) = word;
+    }
+  }
+  {  // value words: four slots share a word; keep the slots not written now
+    const int quad = tid >> 6, c16 = (tid >> 2) & 15, wv = tid & 3;
+    if (4 * quad + 3 >= p_lo && 4 * quad < p_hi) {
+      int sh;
+      const uint32_t off = page_v_offset(4 * quad, 32 * wv + c16, &sh);
+      uint32_t word = (4 * quad < p_lo || 4 * quad + 3 >= p_hi) ? *(const uint32_t*)(page + off) : 0u;
+      for (int i = 0; i < 4; ++i) {
+        const int p = 4 * quad + i;
+        if (p < p_lo || p >= p_hi) continue;
+        for (int hh = 0; hh < 2; ++hh) {
+          const int c = 16 * (2 * wv + hh) + c16;
+          (void)page_v_offset(p, c, &sh);
+          word = (word & ~(0xFu << sh)) | ((uint32_t)cs[1][p][c] << sh);
+        }
+      }
+      *(uint32_t*)(page + off) = word;
+    }
+  }
+}
+
 }  // namespace
 }  // namespace kvq

@@ -910,7 +910,10 @@ template <int NS>
 __global__ __launch_bounds__(256, 2) void paged_split_kernel(DecodeArgs a) {
   __shared__ SplitSmem<NS> sm;
   const int split = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-  const int n2 = max(a.pg.int2_len[r], 0), n4 = max(a.pg.int4_len[r], 0);
+  const int n2 = max(a.pg.int2_len[r], 0), n4_old = max(a.pg.int4_len[r], 0);
+  // a fused append adds INT4 token n4_old (int4_len counts the tokens before
+  // it); the attention covers the lengths a decode after it would see
+  const int n4 = a.k_new != nullptr ? n4_old + 1 : n4_old;
   const int gps = a.groups_per_split;
   const int n2g = n2 / GS, n4g = (n4 + GS - 1) / GS, full4 = n4 / GS;
   const int s2 = (n2g + gps - 1) / gps;  // splits of the INT2 part
@@ -926,7 +929,22 @@ __global__ __launch_bounds__(256, 2) void paged_split_kernel(DecodeArgs a) {
     const int i = split - s2;
     const int g0 = i < s4 ? i * gps : n4g;
     const int g1 = i < s4 - 1 ? g0 + gps : n4g;
-    paged_int4_split<NS>(a, sm, r, h, split, g0, g1, n4, table + n2 / PAGE_TOKENS);
+    const int32_t* table4 = table + n2 / PAGE_TOKENS;
+    if (a.k_new != nullptr && n4_old / GS >= g0 && n4_old / GS < g1) {
+      // this workgroup reads the pair the new token goes to: write the token
+      // into its INT4 page (per-token codes and meta, as the append kernel
+      // does) before any wave loads that pair
+      const int tid = threadIdx.x, slot = n4_old % PAGE_TOKENS;
+      const size_t sigma = (size_t)r * a.geo.hkv + h;
+      sm.flush.xs[tid >> 7][slot][tid & 127] = (tid < 128 ? a.k_new : a.v_new)[sigma * D + (tid & 127)];
+      __syncthreads();
+      uint8_t* page = a.geo.base + a.pg.int4_offset +
+                      (size_t)(table4[n4_old / PAGE_TOKENS] - a.pg.int2_pages) * a.pg.int4_page_bytes +
+                      (size_t)h * INT4_HEAD;
+      page_append_int4(page, sm.flush.xs, sm.flush.cs, slot, slot + 1, tid);
+      __syncthreads();
+    }
+    paged_int4_split<NS>(a, sm, r, h, split, g0, g1, n4, table4);
   }
 }
 

@@ -1,7 +1,7 @@
 """Parity at full size. The benchmark's workloads are built exactly as the benchmark builds them
 (a subset of their layers: each built layer has the benchmark's shapes, data, split count and
 launches), stepped through their decode cycle with the benchmark's own step (the token append
-fused into the decode split pass for contiguous caches; append, then decode for the paged pool),
+fused into the decode split pass, for contiguous caches and for the paged pool),
 and checked on sampled (request, KV head) streams: packed bytes bit-exact against the oracle's
 packing of the regenerated stream, attention within the stated tolerance of the oracle's fp64
 attention. Every other request of the batch is computed in the same launches. The fused step's

@@ -227,3 +227,41 @@ def test_paged_decode_deterministic(small):
     a = small.decode(0, q)
     b = small.decode(0, q)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_fused_paged_step_equals_separate_calls(small, splits):
+    """kvq_append_decode_attention on a paged pool: three decode steps of requests 0..3 (their
+    new INT4 tokens land in pages the tables already hold) give, bit for bit, the pool bytes,
+    output and log-sum-exp of kvq_quantize_append(n_new = 1) followed by kvq_decode_attention."""
+    c, kvq, B = small, small.kvq, 4
+    pool_a, pool_b = c.pool.clone(), c.pool.clone()
+    n2 = torch.tensor(c.n2[:B], dtype=torch.int32, device="cuda")
+    n4 = torch.tensor(c.n4[:B], dtype=torch.int32, device="cuda")
+    table = c.table[:B].contiguous()
+    for step in range(3):
+        before, after = n4.clone(), n4 + 1
+        ml = max(a + b for a, b in zip(c.n2[:B], c.n4[:B])) + step + 1
+        ws = torch.empty(kvq.workspace_bytes(c.plan, B, ml, splits) // 4 + 1, dtype=torch.float32, device="cuda")
+        for l in range(c.layers):
+            kn = syn.keys_fp16(c.seed + 1, l, range(B), range(c.hkv), 1000 + step, 1, num_kv_heads=c.hkv).cuda()
+            vn = syn.values_fp16(c.seed + 1, l, range(B), range(c.hkv), 1000 + step, 1).cuda()
+            q = syn.queries_fp16(c.seed + 1, l, step, B, c.hq).cuda()
+            outs = []
+            for fused, pool in ((True, pool_a), (False, pool_b)):
+                out = torch.full((B, c.hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+                lse = torch.full((B, c.hq), float("nan"), dtype=torch.float32, device="cuda")
+                if fused:
+                    pg = kvq.make_pages(table, c.max_pages, n2, before)
+                    kvq.append_decode_attention(c.plan, l, pool, kn, vn, q, None, ml, 1 / math.sqrt(128), out, lse,
+                                                ws, splits, pages=pg)
+                else:
+                    kvq.quantize_append(c.plan, l, pool, kn, vn, None, kvq.make_pages(table, c.max_pages, n2, before))
+                    kvq.decode_attention(c.plan, l, pool, q, None, ml, 1 / math.sqrt(128), out, lse, ws, splits,
+                                         pages=kvq.make_pages(table, c.max_pages, n2, after))
+                torch.cuda.synchronize()
+                outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+            assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1]), (step, l)
+            assert np.isfinite(outs[0][0]).all()
+        assert torch.equal(pool_a, pool_b), f"step {step}: pool bytes differ"
+        n4 = after

@@ -163,7 +163,7 @@ def test_fused_append_decode_argument_errors(lib):
     def call(plan=plan, layer=0, batch=2, max_seq_len=64, ws_bytes=1 << 30, splits=0, seq=True, kn=True):
         return lib.kvq_append_decode_attention(ctypes.byref(plan), layer, f, f if kn else None, f, f,
                                                f if seq else None, batch, max_seq_len, ctypes.c_float(0.088), f, 0,
-                                               None, f, ws_bytes, splits, None)
+                                               None, f, ws_bytes, splits, None, None)
 
     assert call(layer=2) == kvq.ERR_INVALID_ARG
     assert call(batch=5) == kvq.ERR_INVALID_ARG
@@ -173,8 +173,8 @@ def test_fused_append_decode_argument_errors(lib):
     assert call(splits=2000) == kvq.ERR_INVALID_ARG
     assert call(seq=False) == kvq.ERR_INVALID_ARG
     assert call(kn=False) == kvq.ERR_INVALID_ARG
-    assert call(plan=_paged_plan()) == kvq.ERR_UNSUPPORTED
-    assert "paged" in lib.kvq_last_error().decode()
+    assert call(plan=_paged_plan()) == kvq.ERR_INVALID_ARG  # a paged plan needs pages
+    assert "pages" in lib.kvq_last_error().decode()
     assert call(batch=0) == kvq.OK  # nothing to do
 
 
@@ -215,6 +215,17 @@ def test_paged_argument_errors(lib):
     assert lib.kvq_dequantize(P, 0, f, None, 2, 30, f, f, None, None) == kvq.ERR_INVALID_ARG
     assert lib.kvq_dequantize(P, 0, f, None, 2, 128 * 16 + 1, f, f, ctypes.byref(pages), None) == kvq.ERR_CAPACITY
 
+    def fused(pg, max_seq_len=64, splits=0):
+        return lib.kvq_append_decode_attention(P, 0, f, f, f, f, None, 2, max_seq_len, ctypes.c_float(0.088), f, 0,
+                                               None, f, 1 << 30, splits, ctypes.byref(pg) if pg else None, None)
+
+    assert fused(None) == kvq.ERR_INVALID_ARG  # a paged plan needs pages
+    assert fused(pages, splits=1) == kvq.ERR_INVALID_ARG  # one kind per split: at least 2
+    assert fused(pages, max_seq_len=128 * 16 + 1) == kvq.ERR_CAPACITY
+    assert fused(pages, max_seq_len=0) == kvq.ERR_INVALID_ARG  # it counts the appended token
+    assert fused(kvq.make_pages(_Fake(), 128, _Fake(), _Fake(), _Fake())) == kvq.ERR_INVALID_ARG  # int2_add
+    assert "int2_add" in lib.kvq_last_error().decode()
+
 
 @pytest.mark.parametrize("batch,max_seq_len", [(16, 32768), (1, 32768), (64, 100), (4, 1), (2, 0)])
 def test_paged_auto_splits_hold_the_limits(batch, max_seq_len):
@@ -240,7 +251,7 @@ def test_misaligned_pointers_are_rejected(lib):
     assert lib.kvq_decode_attention(P, 0, f, odd, f, 2, 64, ctypes.c_float(0.088), f, 0, None, f, 1 << 30, 0,
                                     None, None) == kvq.ERR_INVALID_ARG
     assert lib.kvq_append_decode_attention(P, 0, f, f, odd, f, f, 2, 64, ctypes.c_float(0.088), f, 0, None, f,
-                                           1 << 30, 0, None) == kvq.ERR_INVALID_ARG
+                                           1 << 30, 0, None, None) == kvq.ERR_INVALID_ARG
 
 
 def test_prefix_attention_argument_errors(lib):
