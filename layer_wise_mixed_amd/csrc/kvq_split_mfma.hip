@@ -849,9 +849,71 @@ __device__ __forceinline__ void paged_int2_split(const DecodeArgs& a, SplitSmem<
   finish<2, NS>(a, rows, split, wave, sm, ln, acc);
 }
 
+// Fused append in a paged pool: one wave writes a new token into slot p of
+// its KV head's share of an INT4 page (per-token 4-bit codes and meta, the
+// same arithmetic and layout as the append kernel, TriAxialKV page, "Facts":
+// decoded tokens take the INT4 per-token path). Lanes 8g .. 8g + 7 quantize
+// group g (tensor g / 4, channel group g % 4), four channels a lane; the codes
+// meet in the wave's LDS scratch (256 bytes) for the packing. Value words
+// hold four slots: only this slot's nibbles change.
+__device__ __forceinline__ void append_int4_token_wave(uint8_t* page, const uint16_t* kn, const uint16_t* vn, int p,
+                                                       int lane, uint8_t* scratch) {
+  const int g = lane >> 3, tensor = g >> 2, n = g & 3, sub = lane & 7;
+  const int c0 = 32 * n + 4 * sub;
+  typedef uint16_t us4_t __attribute__((ext_vector_type(4)));
+  const us4_t raw = *(const us4_t*)((tensor ? vn : kn) + c0);
+  float x[4], mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = h2f(raw[i]);
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, d));
+    mx = fmaxf(mx, __shfl_xor(mx, d));
+  }
+  const float s = __fdiv_rn(__fsub_rn(mx, mn), 15.0f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float r = 0.f;
+    if (s != 0.0f) r = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x[i], mn), s)), 0.0f), 15.0f);
+    scratch[128 * tensor + c0 + i] = (uint8_t)r;
+  }
+  if (sub == 0) {
+    float* meta = (float*)(page + (tensor ? INT4_VMETA : INT4_KMETA));
+    meta[16 * n + p] = s;
+    meta[64 + 16 * n + p] = mn;
+  }
+  wave_sync_lds();
+  if (lane < 16) {  // key word (a4, w): the 8 codes of channels 32w + 8a4 .. + 7, this slot only
+    const int a4 = lane >> 2, w = lane & 3;
+    uint32_t word = 0;
+#pragma unroll
+    for (int pos = 0; pos < 8; ++pos)
+      word |= (uint32_t)scratch[32 * w + 8 * a4 + pos] << (16 * (pos & 1) + 4 * (pos >> 1));
+    int sh;
+    *(uint32_t*)(page + page_k_offset(p, 32 * w + 8 * a4, &sh)) = word;
+  }
+  {  // value word (channel c % 16 = lane % 16, u / 2 = lane / 16): channels 16u + c15 for u = 2(lane/16), + 1
+    const int c15 = lane & 15, uh = lane >> 4;
+    int sh;
+    const uint32_t off = page_v_offset(p, 16 * (2 * uh) + c15, &sh);
+    uint32_t word = *(const uint32_t*)(page + off);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = 16 * (2 * uh + e) + c15;
+      (void)page_v_offset(p, c, &sh);
+      word = (word & ~(0xFu << sh)) | ((uint32_t)scratch[128 + c] << sh);
+    }
+    *(uint32_t*)(page + off) = word;
+  }
+}
+
 template <int NS>
 __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<NS>& sm, int r, int h, int split,
-                                                 int g0, int g1, int n4, const int32_t* table) {
+                                                 int g0, int g1, int n4, int n4_old, const int32_t* table) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   Lane ln;
@@ -872,8 +934,28 @@ __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<
   src.ida = lane < nk ? region(2 * gi) : 0;
   src.idb = lane < nk ? region(2 * gi + 1) : 0;
   const HeadRows rows{a.q, (size_t)r * a.geo.hq + h * a.geo.g};
-  run_groups<4, 4, true, NS, 1>(src, nk, kmeta, vmeta, ln, acc,
-                                [&] { setup_lane<NS, true>(a, a.geo.g, rows, sm.q, ln, acc); });
+  // fused append: the wave that reads the new token's pair writes the token,
+  // and no other wave reads that pair. run_groups issues the loads of the
+  // wave's first group before setup(): when that group is the pair, the
+  // token goes in first; otherwise while the first group loads. The fence
+  // completes the writes before the wave's later loads.
+  const int pn = n4_old / GS;
+  const bool own = a.k_new != nullptr && pn >= g0 && pn < g1 && ((pn - g0) & (kWaves - 1)) == wave;
+  const bool early = own && pn == first && pn < qend;
+  auto append = [&] {
+    const size_t sigma = (size_t)r * a.geo.hkv + h;
+    uint8_t* page = a.geo.base + a.pg.int4_offset +
+                    (size_t)(table[n4_old / PAGE_TOKENS] - a.pg.int2_pages) * a.pg.int4_page_bytes +
+                    (size_t)h * INT4_HEAD;
+    append_int4_token_wave(page, a.k_new + sigma * D, a.v_new + sigma * D, n4_old % PAGE_TOKENS, lane,
+                           reinterpret_cast<uint8_t*>(vmeta));
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  };
+  if (early) append();
+  run_groups<4, 4, true, NS, 1>(src, nk, kmeta, vmeta, ln, acc, [&] {
+    setup_lane<NS, true>(a, a.geo.g, rows, sm.q, ln, acc);
+    if (own && !early) append();
+  });
 
   // the last, partly filled pair (same units as the full ones), by its wave
   const int pg = full;
@@ -930,21 +1012,7 @@ __global__ __launch_bounds__(256, 2) void paged_split_kernel(DecodeArgs a) {
     const int g0 = i < s4 ? i * gps : n4g;
     const int g1 = i < s4 - 1 ? g0 + gps : n4g;
     const int32_t* table4 = table + n2 / PAGE_TOKENS;
-    if (a.k_new != nullptr && n4_old / GS >= g0 && n4_old / GS < g1) {
-      // this workgroup reads the pair the new token goes to: write the token
-      // into its INT4 page (per-token codes and meta, as the append kernel
-      // does) before any wave loads that pair
-      const int tid = threadIdx.x, slot = n4_old % PAGE_TOKENS;
-      const size_t sigma = (size_t)r * a.geo.hkv + h;
-      sm.flush.xs[tid >> 7][slot][tid & 127] = (tid < 128 ? a.k_new : a.v_new)[sigma * D + (tid & 127)];
-      __syncthreads();
-      uint8_t* page = a.geo.base + a.pg.int4_offset +
-                      (size_t)(table4[n4_old / PAGE_TOKENS] - a.pg.int2_pages) * a.pg.int4_page_bytes +
-                      (size_t)h * INT4_HEAD;
-      page_append_int4(page, sm.flush.xs, sm.flush.cs, slot, slot + 1, tid);
-      __syncthreads();
-    }
-    paged_int4_split<NS>(a, sm, r, h, split, g0, g1, n4, table4);
+    paged_int4_split<NS>(a, sm, r, h, split, g0, g1, n4, n4_old, table4);
   }
 }
 

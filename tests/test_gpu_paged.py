@@ -229,17 +229,16 @@ def test_paged_decode_deterministic(small):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("splits", [0, 3])
-def test_fused_paged_step_equals_separate_calls(small, splits):
-    """kvq_append_decode_attention on a paged pool: three decode steps of requests 0..3 (their
-    new INT4 tokens land in pages the tables already hold) give, bit for bit, the pool bytes,
-    output and log-sum-exp of kvq_quantize_append(n_new = 1) followed by kvq_decode_attention."""
-    c, kvq, B = small, small.kvq, 4
+def _fused_vs_separate(c, B, splits, steps=3):
+    """steps one-token decode appends for requests 0 .. B-1: kvq_append_decode_attention on one
+    copy of the pool against kvq_quantize_append(n_new = 1) then kvq_decode_attention on another;
+    pool bytes, output and log-sum-exp must agree bit for bit."""
+    kvq = c.kvq
     pool_a, pool_b = c.pool.clone(), c.pool.clone()
     n2 = torch.tensor(c.n2[:B], dtype=torch.int32, device="cuda")
     n4 = torch.tensor(c.n4[:B], dtype=torch.int32, device="cuda")
     table = c.table[:B].contiguous()
-    for step in range(3):
+    for step in range(steps):
         before, after = n4.clone(), n4 + 1
         ml = max(a + b for a, b in zip(c.n2[:B], c.n4[:B])) + step + 1
         ws = torch.empty(kvq.workspace_bytes(c.plan, B, ml, splits) // 4 + 1, dtype=torch.float32, device="cuda")
@@ -265,3 +264,41 @@ def test_fused_paged_step_equals_separate_calls(small, splits):
             assert np.isfinite(outs[0][0]).all()
         assert torch.equal(pool_a, pool_b), f"step {step}: pool bytes differ"
         n4 = after
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_fused_paged_step_equals_separate_calls(small, splits):
+    """kvq_append_decode_attention on a paged pool: three decode steps of requests 0..3 (their
+    new INT4 tokens land in pages the tables already hold) give, bit for bit, the pool bytes,
+    output and log-sum-exp of kvq_quantize_append(n_new = 1) followed by kvq_decode_attention."""
+    _fused_vs_separate(small, 4, splits)
+
+
+@pytest.fixture(scope="module")
+def bounds(gpu, oq):
+    # INT4 lengths 30, 31, 127 and 159 (after 64 INT2 tokens): the fused steps write tokens
+    # that complete a page pair (31, 127: the pair is then the first one its wave reads), open
+    # a new pair (32) and land in a wave's second pair (159, one split); every table is then
+    # extended by unused INT4 pages to hold three more tokens
+    calls = [([0], 30, 0), ([1], 31, 0), ([2], 127, 0), ([3], 64 + 159, 64)]
+    c = PagedCase(gpu, oq, hq=8, hkv=2, batch=4, int2_pages=8, int4_pages=32, max_pages=16, calls=calls, seed=12,
+                  layers=1)
+    used = {p for r in range(c.batch) for p in c.quads[r]}
+    free = [p for p in range(c.int2_pages, c.int2_pages + c.int4_pages) if p not in used]
+    for r in range(c.batch):
+        have = len(c.pairs[r]) * 2 + len(c.quads[r])
+        need = -(-(c.n4[r] + 3) // PAGE) - len(c.quads[r])
+        for i in range(need):
+            c.table[r, have + i] = free.pop()
+    return c
+
+
+def test_bounds_lengths(bounds):
+    assert bounds.n2 == [0, 0, 0, 64] and bounds.n4 == [30, 31, 127, 159]
+
+
+@pytest.mark.parametrize("splits", [0, 2, 3])
+def test_fused_paged_step_at_pair_boundaries(bounds, splits):
+    """The fused paged step where the new token completes a page pair, opens one, or lands in
+    a pair its wave reads second: bit for bit the separate calls' pool, output and lse."""
+    _fused_vs_separate(bounds, 4, splits)
