@@ -745,10 +745,26 @@ __device__ __forceinline__ void merge_new_token(uint8_t* tail, const uint16_t* k
 template <int VB, int NS>
 __device__ __forceinline__ void tail_pass(uint8_t* rec, int T, const uint16_t* kn, const uint16_t* vn,
                                           float* kmeta, float* vmeta, const Lane& ln, Acc& acc) {
+  // only the 16-byte pieces that hold a token below T come from their own
+  // address: key row k (words 4k .. 4k+3) of lane l holds token 16 (k / 4) +
+  // l % 16, every value row of lane l tokens 4 (l / 16) + 0..3 and 16 more.
+  // The other lanes read the record's first piece (one line for all; the tail
+  // masking ignores what they get), so no load waits on a lane condition.
   uint32_t kw[32], vw[32];
-  load_codes<16>(rec, ln.lane, kw);
-  load_codes<16>(rec + 8192, ln.lane, vw);
-  if (kn) merge_new_token(rec, kn, vn, T - 1, ln.lane, kw, vw);
+  const int lane = ln.lane;
+  const uint32_t voff = 4 * (lane >> 4) < T ? 8192u + lane * 16u : 0u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t koff = 16 * (k >> 2) + (lane & 15) < T ? k * 1024u + lane * 16u : 0u;
+    const u4_t x = __builtin_nontemporal_load((const u4_t*)(rec + koff));
+    const u4_t y = __builtin_nontemporal_load((const u4_t*)(rec + (voff ? voff + k * 1024u : 0u)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kw[4 * k + i] = x[i];
+      vw[4 * k + i] = y[i];
+    }
+  }
+  if (kn) merge_new_token(rec, kn, vn, T - 1, lane, kw, vw);
   if constexpr (VB < 16) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
