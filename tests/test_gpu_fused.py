@@ -80,6 +80,42 @@ def test_fused_equals_separate_calls_and_oracle(gpu, oq, hq, hkv, splits):
         lens = after
 
 
+def test_fused_every_tail_slot(gpu, oq):
+    """One fused step per tail slot: the new token lands in slot 0 .. 30 of the tail (or
+    completes the group), which the split pass merges into the tail pieces it reads; bit for
+    bit the separate calls, and within the oracle's tolerance."""
+    lens = [64 + t for t in range(32)]
+    cfgs = [(8, 8), (4, 2), (16, 16)]
+    a = Case(gpu, oq, hq=8, hkv=2, batch=len(lens), cap=100, cfgs=cfgs, lens=lens, seed=15)
+    b = Case(gpu, oq, hq=8, hkv=2, batch=len(lens), cap=100, cfgs=cfgs, lens=lens, seed=15)
+    after = [L + 1 for L in lens]
+    seq_before = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    seq_after = torch.tensor(after, dtype=torch.int32, device="cuda")
+    outs = []
+    for l in range(len(cfgs)):
+        q = syn.queries_fp16(a.seed, l, 0, a.batch, 8).cuda()
+        kn, vn = _new_tokens(a, l, lens)
+        out_a, lse_a, ws_a = _buffers(gpu, a, max(after), 0)
+        gpu.append_decode_attention(a.plan, l, a.cache, kn, vn, q, seq_before.clone(), max(after), SCALE, out_a,
+                                    lse_a, ws_a, 0)
+        out_b, lse_b, ws_b = _buffers(gpu, b, max(after), 0)
+        gpu.quantize_append(b.plan, l, b.cache, kn, vn, seq_before.clone())
+        gpu.decode_attention(b.plan, l, b.cache, q, seq_after, max(after), SCALE, out_b, lse_b, ws_b, 0)
+        torch.cuda.synchronize()
+        oa, la, ob, lb = (t.cpu().numpy() for t in (out_a, lse_a, out_b, lse_b))
+        assert np.array_equal(oa, ob) and np.array_equal(la, lb), f"layer {l} {cfgs[l]}"
+        outs.append((q, oa, la))
+    assert torch.equal(a.cache, b.cache)
+    a.lens = after
+    for l in range(len(cfgs)):
+        a.k[l] = syn.keys_fp16(a.seed, l, range(a.batch), range(2), 0, max(after), outlier_count=a.outliers[0],
+                               outlier_factor=a.outliers[1], num_kv_heads=2)
+        a.v[l] = syn.values_fp16(a.seed, l, range(a.batch), range(2), 0, max(after))
+        q, oa, la = outs[l]
+        ref, ref_lse = a.oracle_decode(l, q)
+        check_attention(oa, la, ref, ref_lse, after, 8)
+
+
 def test_fused_packed_groups_match_oracle_packing(gpu, oq):
     """The groups the fused pass completes are packed exactly as the oracle packs them."""
     c = Case(gpu, oq, hq=8, hkv=2, batch=3, cap=96, cfgs=[(4, 2), (8, 4, 1)], lens=[31, 63, 95], seed=4)

@@ -174,6 +174,24 @@ def test_decode_deterministic(ragged):
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
+def test_every_tail_length(gpu, oq):
+    # one request per tail length 0..31 after two packed groups: the split pass reads only the
+    # tail's 16-byte pieces that hold tokens (key rows by token, value rows by groups of four
+    # tokens), so every boundary (T = 4, 5, 16, 17, ...) is one of these rows
+    lens = [64 + t for t in range(32)] + [16, 17]
+    c = Case(gpu, oq, hq=8, hkv=2, batch=len(lens), cap=96, cfgs=[(8, 8), (4, 2), (2, 4, 1), (16, 16)], lens=lens,
+             seed=14)
+    for l in range(len(c.cfgs)):
+        for splits in (0, 2):
+            q = syn.queries_fp16(c.seed, l, splits, c.batch, c.hq).cuda()
+            out, lse = c.decode(l, q, splits)
+            ref, ref_lse = c.oracle_decode(l, q)
+            try:
+                check_attention(out, lse, ref, ref_lse, c.lens, c.hq)
+            except AssertionError as e:
+                raise AssertionError(f"layer {l} {c.cfgs[l]} splits {splits}: {e}") from None
+
+
 @pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 2), (7, 1), (28, 4)])
 def test_gqa_shapes(gpu, oq, hq, hkv):
     c = Case(gpu, oq, hq=hq, hkv=hkv, batch=2, cap=130, cfgs=[(8, 4), (4, 2)], lens=[130, 45], seed=5,
