@@ -738,20 +738,17 @@ __device__ __forceinline__ void merge_new_token(uint8_t* tail, const uint16_t* k
       vw[4 * u + w] = vl && w == wsel ? (vw[4 * u + w] & keep) | ((uint32_t)vv[u] << hs) : vw[4 * u + w];
 }
 
-// The fp16 tail (T tokens), after the packed groups (their registers are
-// free by then), by the wave that owns it, in true units: the accumulators go
-// to true units and back. kn/vn (fused append, the token went to the tail):
-// the new token, merged into the tail's registers and stored into its record.
-template <int VB, int NS>
-__device__ __forceinline__ void tail_pass(uint8_t* rec, int T, const uint16_t* kn, const uint16_t* vn,
-                                          float* kmeta, float* vmeta, const Lane& ln, Acc& acc) {
+// The fp16 tail (T tokens) from its words kw/vw, by the wave that owns it,
+// in true units: the accumulators go to true units and back. kn/vn (fused
+// append, the token went to the tail): the new token, merged into the tail's
+// registers and stored into its record.
+// The tail record's words for a lane (K16V16 layout) into kw/vw.
+__device__ __forceinline__ void load_tail(const uint8_t* rec, int T, int lane, uint32_t* kw, uint32_t* vw) {
   // only the 16-byte pieces that hold a token below T come from their own
   // address: key row k (words 4k .. 4k+3) of lane l holds token 16 (k / 4) +
   // l % 16, every value row of lane l tokens 4 (l / 16) + 0..3 and 16 more.
   // The other lanes read the record's first piece (one line for all; the tail
   // masking ignores what they get), so no load waits on a lane condition.
-  uint32_t kw[32], vw[32];
-  const int lane = ln.lane;
   const uint32_t voff = 4 * (lane >> 4) < T ? 8192u + lane * 16u : 0u;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -764,6 +761,12 @@ __device__ __forceinline__ void tail_pass(uint8_t* rec, int T, const uint16_t* k
       vw[4 * k + i] = y[i];
     }
   }
+}
+
+template <int VB, int NS>
+__device__ __forceinline__ void tail_pass(uint8_t* rec, int T, const uint16_t* kn, const uint16_t* vn, uint32_t* kw,
+                                          uint32_t* vw, float* kmeta, float* vmeta, const Lane& ln, Acc& acc) {
+  const int lane = ln.lane;
   if (kn) merge_new_token(rec, kn, vn, T - 1, lane, kw, vw);
   if constexpr (VB < 16) {
 #pragma unroll
@@ -826,19 +829,39 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   float* kmeta = &sm.loop.kmeta[wave][0][0];
   float* vmeta = sm.loop.vmeta[wave];
 
-  // the wave's packed groups: g0 + wave + 4 k
-  const int first = g0 + wave;
+  // The wave's packed groups: g0 + wave + 4 k, and the tail (if this split
+  // has it) by wave (nq - g0) % 4 after its groups. A short split (at most
+  // two groups a wave) gives the tail wave no packed groups instead: the other
+  // three waves share them, g0 + i + 3 k for the i-th of them, and the tail
+  // wave loads the tail at once, so that it does not start its tail only
+  // when the others are done.
   const int qend = min(g1, nq);
-  const int nk = first < qend ? (qend - first + kWaves - 1) / kWaves : 0;
+  const bool has_tail = T > 0 && nq >= g0 && nq < g1;
+  const int tail_wave = (nq - g0) & (kWaves - 1);
+  const bool own_tail = has_tail && wave == tail_wave;
+  const bool solo = has_tail && qend - g0 <= 2 * kWaves;
+  const int ways = solo ? kWaves - 1 : kWaves;
+  const int first = solo ? (own_tail ? qend : g0 + wave - (wave > tail_wave)) : g0 + wave;
+  const int nk = first < qend ? (qend - first + ways - 1) / ways : 0;
   StreamSrc<KB, VB> src;
   src.first = stream + (size_t)first * g.record_bytes;
-  src.stride = (uint32_t)(kWaves * g.record_bytes);
+  src.stride = (uint32_t)(ways * g.record_bytes);
   src.parts = record_parts(KB, VB);
   const HeadRows rows{a.q, (size_t)r * g.hq + h * g.g};
-  run_groups<KB, VB, KTOK, NS, R>(src, nk, kmeta, vmeta, ln, acc,
-                                  [&] { setup_lane<NS, KTOK && KB < 16>(a, g.g, rows, sm.q, ln, acc); });
-  if (T > 0 && nq >= g0 && nq < g1 && ((nq - g0) & (kWaves - 1)) == wave)
-    tail_pass<VB, NS>(stream + g.tail_offset, T, kn, vn, kmeta, vmeta, ln, acc);
+  uint8_t* tail = stream + g.tail_offset;
+  uint32_t tkw[32], tvw[32];
+  if (own_tail && nk == 0) {
+    load_tail(tail, T, threadIdx.x & 63, tkw, tvw);
+    setup_lane<NS, KTOK && KB < 16>(a, g.g, rows, sm.q, ln, acc);
+    tail_pass<VB, NS>(tail, T, kn, vn, tkw, tvw, kmeta, vmeta, ln, acc);
+  } else {
+    run_groups<KB, VB, KTOK, NS, R>(src, nk, kmeta, vmeta, ln, acc,
+                                    [&] { setup_lane<NS, KTOK && KB < 16>(a, g.g, rows, sm.q, ln, acc); });
+    if (own_tail) {
+      load_tail(tail, T, threadIdx.x & 63, tkw, tvw);
+      tail_pass<VB, NS>(tail, T, kn, vn, tkw, tvw, kmeta, vmeta, ln, acc);
+    }
+  }
   finish<VB, NS>(a, rows, split, wave, sm, ln, acc);
 }
 
