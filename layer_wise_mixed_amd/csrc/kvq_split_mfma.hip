@@ -346,8 +346,8 @@ __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t
 
 // Every member is a multiple of 16 bytes long, so with the struct aligned
 // each member is too (LDS reads of q', meta and results stay 16 bytes wide).
-// The meta staging of the group loop and the per-wave results of the combine
-// share storage: the combine starts after a barrier that ends every loop.
+// The per-wave results of the combine have storage of their own, so a wave
+// writes its result as soon as it is done, and one barrier starts the combine.
 template <int R>
 struct alignas(16) SplitSmem {
   struct Loop {
@@ -360,9 +360,9 @@ struct alignas(16) SplitSmem {
   };
   union {
     Loop loop;
-    float o[kWaves][kMaxG][D];  // per wave: its result, for the combine
     Flush flush;
   };
+  float o[kWaves][kMaxG][D];  // per wave: its result, for the combine
   float ml[kWaves][2][kMaxG];
   float q[kMaxG][D];  // q' of the G query rows (every wave writes the same values)
 };
@@ -436,7 +436,6 @@ __device__ __forceinline__ void finish(const DecodeArgs& a, const HeadRows& rows
   const int G = ln.g;
   const float l = sum_lane_groups(acc.lpart);
   const float vmul = code_scale<VB>();
-  __syncthreads();  // every wave is out of its group loop: sm.o may reuse the meta staging
 #pragma unroll
   for (int pass = 0; pass < 4 / NS; ++pass) {
     const float z = sum_lane_groups(acc.zpart[pass]);
