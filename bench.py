@@ -72,10 +72,13 @@ PAGED_WORKLOADS = {
     "paged-b16-l32768-int2int4": dict(layers=36, hq=32, hkv=8, batch=16, prefill=32767, cycle=32,
                                       outliers=(4, 10.0),
                                       desc="36 layers, 32/8 heads, batch 16, context 32768..32799 in a paged pool: "
-                                           "16384 INT2 tokens (seeded 32-token runs) + INT4 rest, 3.0 bits"),
+                                           "16384 INT2 tokens (seeded 32-token runs) + 16384..16415 INT4 tokens, "
+                                           "3.0 bits at context 32768"),
 }
 WORKLOADS.update({k: dict(v, paged=True) for k, v in PAGED_WORKLOADS.items()})
-DEFAULT_WORKLOAD = "llama31-8b-b64-kivi8-trace"
+DEFAULT_WORKLOAD = "llama31-8b-b64-mixed325-l2048"
+# timed beside the headline, in the same JSON line: the uniform K8V8 (KIVI-8-like) baseline
+SECONDARY_WORKLOAD = "llama31-8b-b64-kivi8-trace"
 
 
 def capacity(w):
@@ -267,7 +270,9 @@ class PagedWorkload:
         self.outliers = w["outliers"]
         self.scale = 1.0 / math.sqrt(128.0)
         runs = self.P // 32
-        self.n2 = 32 * (runs // 2)  # INT2 tokens per request: half of the prompt's 32-token runs
+        # INT2 tokens per request: 512 of the prompt's 1023 full 32-token runs, 16384 tokens, so that
+        # at the first decode step half of the cache (16384 of 32768 tokens) is INT2: 3.0 bits
+        self.n2 = 32 * ((runs + 1) // 2)
         n4_cap = self.P - self.n2 + self.C
         pairs_per_req = self.n2 // 32
         quads_per_req = -(-n4_cap // self.PAGE)
@@ -379,16 +384,17 @@ def _source_hash():
     return h.hexdigest()[:16]
 
 
-def _traffic(workload, achieved_bytes_per_launch):
-    """HBM bytes per split launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources; else None."""
+def _traffic(workload, window):
+    """HBM bytes per split launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources over the same window of cycle positions as this run's timed
+    steps (`window` = [first, last] position, every position between them timed); else None."""
     path = os.path.join(ROOT, "profiles", "split_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
         e = d.get(workload)
-        if not e or e.get("source_hash") != _source_hash():
+        if not e or e.get("source_hash") != _source_hash() or e.get("window") != list(window):
             return None
         return e["hbm_bytes_per_launch"]
     except Exception:
@@ -396,60 +402,81 @@ def _traffic(workload, achieved_bytes_per_launch):
 
 
 # -------------------------------------------------------------- CPU baseline
-def cpu_baseline_paged(wl, max_seconds=20.0):
-    """The oracle on a sample of the last decode step of a paged workload: it packs a sample of
-    (request, KV head) streams of layer 0 into its own pool through the same page tables, then
-    times unpack + dequantize + fp64 attention."""
+def _timed_reps(fn, max_seconds, max_reps=1000):
+    """Call fn() until about max_seconds have passed: (seconds per call, calls, fn's last result)."""
+    t0 = time.perf_counter()
+    reps, res = 0, None
+    while True:
+        res = fn()
+        reps += 1
+        if time.perf_counter() - t0 > max_seconds or reps >= max_reps:
+            break
+    return (time.perf_counter() - t0) / reps, reps, res
+
+
+def _threads():
+    return min(os.cpu_count() or 1, 16)
+
+
+def cpu_baseline_paged(wl, positions, max_seconds=15.0):
+    """The oracle on a sample of the timed decode steps of a paged workload: it packs a sample of
+    (request, KV head) streams of layer 0 into its own pool through the same page tables, each
+    stream at the INT4 length of one of the timed cycle positions, then times unpack +
+    dequantize + fp64 attention on all host threads (up to 16) and on one thread."""
     import numpy as np
 
     import oracle
 
-    n4 = wl.P - wl.n2 + wl.C  # INT4 tokens at the last step of the cycle
     G = wl.Hq // wl.Hkv
     layer = wl.layer_ids[0]
     n_streams = min(wl.B * wl.Hkv, 16)
     pool = np.zeros(oracle.paged_pool_bytes(wl.Hkv, wl.int2_pages, wl.int4_pages), np.uint8)
     tables = wl.table.cpu().numpy()
     cnt, fac = wl.outliers
-    req, head, qs = [], [], np.zeros((n_streams, G, 128), np.float16)
+    req, head, n4s, qs = [], [], [], np.zeros((n_streams, G, 128), np.float16)
     for s in range(n_streams):
         r, h = divmod(s, wl.Hkv)
-        order = wl._prompt_order(r) + list(range(wl.P, wl.P + wl.C))
-        k = syn.keys_fp16(wl.seed, layer, [r], [h], 0, wl.P + wl.C, outlier_count=cnt, outlier_factor=fac,
+        pos = positions[s % len(positions)]
+        n4 = wl.P - wl.n2 + pos + 1
+        order = wl._prompt_order(r) + list(range(wl.P, wl.P + pos + 1))
+        k = syn.keys_fp16(wl.seed, layer, [r], [h], 0, wl.P + pos + 1, outlier_count=cnt, outlier_factor=fac,
                           num_kv_heads=wl.Hkv)[0, 0].numpy()[order]
-        v = syn.values_fp16(wl.seed, layer, [r], [h], 0, wl.P + wl.C)[0, 0].numpy()[order]
+        v = syn.values_fp16(wl.seed, layer, [r], [h], 0, wl.P + pos + 1)[0, 0].numpy()[order]
         oracle.pack_paged(pool, k, v, wl.n2, tables[r], wl.int2_pages, wl.Hkv, h)
         req.append(r)
         head.append(h)
-        qs[s] = syn.queries_fp16(wl.seed, layer, wl.C - 1, r + 1, wl.Hq)[r, h * G:(h + 1) * G].numpy()
-    threads = min(os.cpu_count() or 1, 16)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        _, _, used = oracle.decode_paged(pool, req, head, [wl.n2] * n_streams, [n4] * n_streams, tables,
-                                         wl.int2_pages, wl.Hkv, qs, G, wl.scale, threads)
-        reps += 1
-        if time.perf_counter() - t0 > max_seconds or reps >= 1000:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    t_step = dt / n_streams * wl.B * wl.Hkv * wl.L
+        n4s.append(n4)
+        qs[s] = syn.queries_fp16(wl.seed, layer, pos, r + 1, wl.Hq)[r, h * G:(h + 1) * G].numpy()
+
+    def run(ns, threads):
+        return oracle.decode_paged(pool, req[:ns], head[:ns], [wl.n2] * ns, n4s[:ns], tables, wl.int2_pages,
+                                   wl.Hkv, qs[:ns], G, wl.scale, threads)[2]
+
+    dt, reps, used = _timed_reps(lambda: run(n_streams, _threads()), max_seconds)
+    n1 = min(n_streams, 2)
+    dt1, reps1, _ = _timed_reps(lambda: run(n1, 1), max_seconds / 3)
+    scale = wl.B * wl.Hkv * wl.L
+    t_step, t_step1 = dt / n_streams * scale, dt1 / n1 * scale
     return {"value": wl.B / t_step, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{n_streams} (request, KV head) streams of layer 0 at {wl.n2} INT2 + {n4} INT4 tokens, "
-                      f"repeated {reps}x ({dt * 1e3:.1f} ms each); step time scaled to {wl.B * wl.Hkv} streams x "
-                      f"{wl.L} layers"}
+            "value_1thread": wl.B / t_step1,
+            "sample": f"{n_streams} (request, KV head) streams of layer 0, each at the length of one of the timed "
+                      f"cycle positions ({wl.n2} INT2 + {min(n4s)}..{max(n4s)} INT4 tokens), repeated {reps}x "
+                      f"({dt * 1e3:.1f} ms each) on {int(used)} threads, and {n1} streams {reps1}x on 1 thread; "
+                      f"step time scaled to {wl.B * wl.Hkv} streams x {wl.L} layers"}
 
 
-def cpu_baseline(wl, max_seconds=20.0):
-    """The oracle, timed on host cores on a sample of the last decode step of the cycle:
-    unpack + dequantize its own packed streams, then fp64 attention."""
+def cpu_baseline(wl, positions, max_seconds=15.0):
+    """The oracle, timed on host cores on a sample of the timed decode steps: a sample of (request,
+    KV head) streams of layer 0, each at the cache length of one of the timed cycle positions,
+    packed by the oracle into its own layer; it unpacks + dequantizes them and runs fp64
+    attention, on all host threads (up to 16) and on one thread."""
     import numpy as np
 
     import oracle
 
     if isinstance(wl, PagedWorkload):
-        return cpu_baseline_paged(wl, max_seconds)
+        return cpu_baseline_paged(wl, positions, max_seconds)
 
-    L = wl.P + wl.C  # the last step of the cycle
     G = wl.Hq // wl.Hkv
     layer = wl.layer_ids[0]
     lp = wl.plan.layers[0]
@@ -460,92 +487,53 @@ def cpu_baseline(wl, max_seconds=20.0):
     n_streams = min(wl.B * wl.Hkv, 64)
     buf = np.zeros(n_streams * stride, np.uint8)
     qs = np.zeros((n_streams, G, 128), np.float16)
+    lens = np.zeros(n_streams, np.int64)
     cnt, fac = wl.outliers
     for s in range(n_streams):
         r, h = divmod(s, wl.Hkv)
+        pos = positions[s % len(positions)]
+        L = wl.P + pos + 1  # the cache length a decode at this position attends over
         k = syn.keys_fp16(wl.seed, layer, [r], [h], 0, L, outlier_count=cnt, outlier_factor=fac,
                           num_kv_heads=wl.Hkv)[0, 0].numpy()
         v = syn.values_fp16(wl.seed, layer, [r], [h], 0, L)[0, 0].numpy()
         sq = oracle.quantize_stream(k, v, kb, vb, kt)
         b, _ = oracle.pack_stream(sq, cap_groups)
         buf[s * stride:(s + 1) * stride] = b
-        qs[s] = syn.queries_fp16(wl.seed, layer, wl.C - 1, r + 1, wl.Hq)[r, h * G:(h + 1) * G].numpy()
+        lens[s] = L
+        qs[s] = syn.queries_fp16(wl.seed, layer, pos, r + 1, wl.Hq)[r, h * G:(h + 1) * G].numpy()
     ids = np.arange(n_streams, dtype=np.int64)
-    lens = np.full(n_streams, L, np.int64)
-    threads = min(os.cpu_count() or 1, 16)
-    # repeat the sample until about max_seconds of wall time
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        _, _, used = oracle.decode_packed(buf, stride, ids, lens, kb, vb, kt, cap_groups, qs, G, wl.scale, threads)
-        reps += 1
-        if time.perf_counter() - t0 > max_seconds or reps >= 1000:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    per_stream = dt / n_streams
-    t_step = per_stream * wl.B * wl.Hkv * wl.L
+
+    def run(ns, threads):
+        return oracle.decode_packed(buf, stride, ids[:ns], lens[:ns], kb, vb, kt, cap_groups, qs[:ns], G, wl.scale,
+                                    threads)[2]
+
+    dt, reps, used = _timed_reps(lambda: run(n_streams, _threads()), max_seconds)
+    n1 = min(n_streams, 8)
+    dt1, reps1, _ = _timed_reps(lambda: run(n1, 1), max_seconds / 3)
+    scale = wl.B * wl.Hkv * wl.L
+    t_step, t_step1 = dt / n_streams * scale, dt1 / n1 * scale
     return {"value": wl.B / t_step, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{n_streams} (request, KV head) streams of layer 0 at L={L}, repeated {reps}x "
-                      f"({dt * 1e3:.1f} ms each); step time scaled to {wl.B * wl.Hkv} streams x {wl.L} layers"}
+            "value_1thread": wl.B / t_step1,
+            "sample": f"{n_streams} (request, KV head) streams of layer 0 ({lp.k_bits}/{lp.v_bits} bits), each at the "
+                      f"length of one of the timed cycle positions (L = {int(lens.min())}..{int(lens.max())}), "
+                      f"repeated {reps}x ({dt * 1e3:.1f} ms each) on {int(used)} threads, and {n1} streams {reps1}x "
+                      f"on 1 thread; step time scaled to {wl.B * wl.Hkv} streams x {wl.L} layers"}
 
 
 # ---------------------------------------------------------------------- main
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: one decode cycle)")
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--unfused", action="store_true",
-                    help="append with its own launch instead of inside the split pass")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference kernel "
-                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this path has no multi-GPU leg (run with --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def time_workload(wl, K, W, graph=True):
+    """Time K decode steps of `wl` (after W untimed ones): HIP-graph replays between two events on
+    the launch stream, then the same K steps launched eagerly with HIP events bound to each kernel
+    dispatch for the per-kernel roofline. Returns the measured figures."""
     import torch
 
-    import layer_wise_mixed_amd as kvq
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-    if args.copy_calibrate:
-        n = args.copy_calibrate
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "launches": 5}))
-        return
-    kvq.load()
-    t_setup = time.perf_counter()
-    cls = PagedWorkload if WORKLOADS[args.workload].get("paged") else Workload
-    wl = cls(args.workload, seed=args.seed, num_splits=args.splits, fused=not args.unfused)
-    fused = getattr(wl, "fused", False)
-    K = args.steps if args.steps is not None else wl.C
-    W = args.warmup if args.warmup is not None else min(wl.C, 16)
-    print(f"# setup {time.perf_counter() - t_setup:.1f}s: {wl.w['desc']}, splits={wl.splits}", file=sys.stderr,
-          flush=True)
-
+    kvq = wl.kvq
     stream = torch.cuda.Stream()
     graphs = None
     with torch.cuda.stream(stream):
         wl.reset()
         torch.cuda.synchronize()
-        if not args.no_graph:
+        if graph:
             # capture one graph per cycle position; capture itself runs nothing
             graphs = []
             for i in range(min(wl.C, max(K, W, 1))):
@@ -590,63 +578,151 @@ def main():
         merge_ms, merge_n = kvq.timer_read(kvq.TIMER_MERGE)
         app_ms, app_n = kvq.timer_read(kvq.TIMER_APPEND)
         kvq.timer_stop()
-
-    ms_per_step = gpu_ms / K
-    tokens = wl.B * K
-    value = tokens / (gpu_ms / 1e3)
+    del graphs
     positions = [i % wl.C for i in range(K)]
     bytes_total = sum(wl.split_bytes(p) for p in positions)
-    bytes_launches = bytes_total
     n_launch = K * wl.L
     avg_split_s = (split_ms / 1e3) / max(split_n, 1)
-    achieved = (bytes_launches / n_launch) / avg_split_s / 1e9 if split_n else None
-    eff_gbs = bytes_total / (gpu_ms / 1e3) / 1e9
-    traffic = _traffic(args.workload, bytes_launches / max(n_launch, 1))
-    print(f"# {K} steps in {gpu_ms:.3f} ms GPU ({wall * 1e3:.1f} ms wall); split {split_n} launches avg "
-          f"{avg_split_s * 1e6:.2f} us; merge avg {merge_ms / max(merge_n, 1) * 1e3:.2f} us; append avg "
-          f"{app_ms / max(app_n, 1) * 1e3:.2f} us; whole-step effective {eff_gbs:.0f} GB/s", file=sys.stderr,
+    achieved = (bytes_total / n_launch) / avg_split_s / 1e9 if split_n else None
+    window = [min(positions), max(positions)]
+    return {"K": K, "W": W, "gpu_ms": gpu_ms, "wall_s": wall, "ms_per_step": gpu_ms / K,
+            "value": wl.B * K / (gpu_ms / 1e3), "positions": positions, "window": window,
+            "context": [wl.P + 1 + window[0], wl.P + 1 + window[1]],
+            "bytes_total": bytes_total, "bytes_per_launch": bytes_total / max(n_launch, 1),
+            "avg_split_s": avg_split_s, "split_n": split_n, "achieved": achieved,
+            "merge_us": merge_ms * 1e3 / max(merge_n, 1), "merge_n": merge_n,
+            "append_us": app_ms * 1e3 / max(app_n, 1), "append_n": app_n,
+            "eff_gbs": bytes_total / (gpu_ms / 1e3) / 1e9,
+            "traffic": _traffic(wl.name, window), "graph": graphs is not None or graph}
+
+
+def roofline_obj(m, fused):
+    return {"bound": "hbm", "achieved": m["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": (m["achieved"] / HBM_PEAK_GBS) if m["achieved"] else None, "traffic": m["traffic"],
+            "kernel": "decode split pass" + (" (with the fused token append)" if fused else ""),
+            "avg_launch_us": m["avg_split_s"] * 1e6,
+            "timing": "HIP events bound to each split dispatch, eager pass over the same K steps",
+            "bytes_per_launch": m["bytes_per_launch"],
+            "traffic_window": "cycle positions %d..%d" % tuple(m["window"])}
+
+
+def workload_config(wl, m, fused, graph):
+    return {"workload": wl.name, "description": wl.w["desc"], "layers": wl.L, "batch": wl.B,
+            "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": 128, "context": m["context"],
+            "equiv_bits": wl.plan.equiv_bits, "splits": wl.splits,
+            "launch": ("hip-graph per step" if graph else "eager")
+            + ("; token append fused into the split pass" if fused else "; append kernel, then split pass"),
+            "effective_GBps_whole_step": m["eff_gbs"], "effective_frac_whole_step": m["eff_gbs"] / HBM_PEAK_GBS}
+
+
+def make_workload(name, args):
+    cls = PagedWorkload if WORKLOADS[name].get("paged") else Workload
+    return cls(name, seed=args.seed, num_splits=args.splits, fused=not args.unfused)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: one decode cycle)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--secondary", default=None, choices=sorted(WORKLOADS) + ["none"],
+                    help="workload timed after the headline one and reported beside it (default: the "
+                         "uniform K8V8 trace when the headline is the default workload)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--unfused", action="store_true",
+                    help="append with its own launch instead of inside the split pass")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the prefill-append and prefix-attention figures")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU leg (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import layer_wise_mixed_amd as kvq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.copy_calibrate:
+        n = args.copy_calibrate
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+    kvq.load()
+    t_setup = time.perf_counter()
+    wl = make_workload(args.workload, args)
+    fused = getattr(wl, "fused", False)
+    K = args.steps if args.steps is not None else wl.C
+    W = args.warmup if args.warmup is not None else min(wl.C, 16)
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s: {wl.w['desc']}, splits={wl.splits}", file=sys.stderr,
           flush=True)
+    m = time_workload(wl, K, W, graph=not args.no_graph)
+    print(f"# {K} steps in {m['gpu_ms']:.3f} ms GPU ({m['wall_s'] * 1e3:.1f} ms wall); split {m['split_n']} launches "
+          f"avg {m['avg_split_s'] * 1e6:.2f} us ({(m['achieved'] or 0) / HBM_PEAK_GBS:.3f} of HBM peak); merge avg "
+          f"{m['merge_us']:.2f} us; append avg {m['append_us']:.2f} us; whole-step effective {m['eff_gbs']:.0f} GB/s",
+          file=sys.stderr, flush=True)
 
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": m["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 mfma (hi+lo operand parts), f32 accumulate, f16 out",
         "data": "synthetic",
-        "config": {"workload": args.workload, "description": wl.w["desc"], "layers": wl.L, "batch": wl.B,
-                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": 128, "context": [wl.P + 1, wl.P + wl.C],
-                   "equiv_bits": wl.plan.equiv_bits, "splits": wl.splits,
-                   "launch": ("eager" if graphs is None else "hip-graph per step")
-                   + ("; token append fused into the split pass" if fused else "; append kernel, then split pass"),
-                   "effective_GBps_whole_step": eff_gbs, "effective_frac_whole_step": eff_gbs / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": traffic,
-                     "kernel": "decode split pass" + (" (with the fused token append)" if fused else ""),
-                     "avg_launch_us": avg_split_s * 1e6,
-                     "timing": "HIP events bound to each split dispatch, eager pass over the same K steps",
-                     "bytes_per_launch": bytes_launches / max(n_launch, 1)},
+        "config": workload_config(wl, m, fused, not args.no_graph),
+        "roofline": roofline_obj(m, fused),
     }
-    if hasattr(wl, "prefill_append_rate"):
+    if not args.no_extras and hasattr(wl, "prefill_append_rate"):
         # the quantize-and-pack kernel at prefill size (HBM-bound there), reported beside the step
         result["prefill_append"] = wl.prefill_append_rate()
         print(f"# prefill append, layer {result['prefill_append']['layer']}: "
               f"{result['prefill_append']['us']:.1f} us, {result['prefill_append']['GBps']:.0f} GB/s", file=sys.stderr,
               flush=True)
-    if hasattr(wl, "prefix_attention_rate"):
+    if not args.no_extras and hasattr(wl, "prefix_attention_rate"):
         # chunked-prefill attention over the quantized prefix (matrix-core bound), beside the step
         pa = result["prefix_attention"] = wl.prefix_attention_rate()
         print(f"# prefix attention, layer {pa['layer']} {pa['format']}: {pa['rows']} rows x {pa['prefix']} tokens "
               f"in {pa['us']:.1f} us, {pa['TFLOPs']:.0f} TFLOP/s ({100 * pa['frac']:.1f}% of fp16 peak)",
               file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, m["positions"], args.cpu_seconds)
+    sec = args.secondary or (SECONDARY_WORKLOAD if args.workload == DEFAULT_WORKLOAD else "none")
+    if sec != "none" and sec != args.workload:
+        del wl
+        torch.cuda.empty_cache()
+        wl2 = make_workload(sec, args)
+        K2 = wl2.C if args.steps is None else args.steps
+        W2 = min(wl2.C, 16) if args.warmup is None else args.warmup
+        m2 = time_workload(wl2, K2, W2, graph=not args.no_graph)
+        print(f"# secondary {sec}: {K2} steps, {m2['value']:.0f} tokens/s, split avg {m2['avg_split_s'] * 1e6:.2f} us "
+              f"({(m2['achieved'] or 0) / HBM_PEAK_GBS:.3f} of HBM peak)", file=sys.stderr, flush=True)
+        result["secondary"] = {"value": m2["value"], "unit": "tokens/s", "steps": K2, "warmup": W2,
+                               "ms_per_step": m2["ms_per_step"],
+                               "config": workload_config(wl2, m2, fused, not args.no_graph),
+                               "roofline": roofline_obj(m2, fused)}
     print(json.dumps(result), flush=True)
 
 

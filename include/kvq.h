@@ -19,9 +19,12 @@
  *    thread). Nothing throws or aborts across the ABI. Kernels run
  *    asynchronously on the given stream (a hipStream_t; NULL = the null
  *    stream).
- *  - Values that live on the device (sequence lengths, page ids) are trusted
- *    as far as the cache contents go; kernels never write outside the cache
- *    region of the layer they were given.
+ *  - Values that live on the device (sequence lengths, page ids) are checked
+ *    before every write: a length past the planned capacity, or a page-table
+ *    entry that is out of range or names a page of the wrong pool, makes the
+ *    kernel skip that write, so no kernel writes outside the cache region of
+ *    the layer it was given. Reads trust them: a decode over a bad page table
+ *    reads whatever the ids point at.
  *  - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
  *  - head_dim is 128 and the quantization group is 32 (elements of a group:
  *    32 tokens of one channel for per-channel keys, 32 channels of one token
@@ -119,8 +122,10 @@ typedef struct kvq_plan {
  * 2i = its even id P and entry 2i+1 = P + 1. The next ceil(int4_len/16)
  * entries hold the INT4 pages (keys and values per-token, 4 bits), entry
  * int2_len/16 + t/16 holding INT4 token t. A request's tokens are its INT2
- * tokens, then its INT4 tokens. Ids and lengths are trusted: the library
- * does not check them on the device. */
+ * tokens, then its INT4 tokens. The appends check every entry they write
+ * through (entry below max_pages_per_req; an INT2 pair id even and below
+ * int2_pages; an INT4 id in [int2_pages, int2_pages + int4_pages)) and skip
+ * the write otherwise; the decode passes read through the ids unchecked. */
 typedef struct kvq_pages {
     const int32_t *page_table; /* [batch][max_pages_per_req] */
     int32_t max_pages_per_req;
@@ -300,7 +305,12 @@ int kvq_prefix_attention(const kvq_plan *plan, int32_t layer, const void *cache,
  * k_out, v_out: device fp32 [batch][Hkv][max_seq_len][128]; token j of
  * request r is fmaf(code, scale, zero) for quantized tokens and the stored
  * fp16 value for tail tokens; rows at or past the request's length are not
- * written. Paged mode (pages != NULL; seq_lens ignored) lists each
+ * written. The codes, scales and zero points are those of the asymmetric
+ * groupwise quantizer (TriAxialKV page, "Facts", quantizer bullet: one
+ * scale and zero point per group of 32, keys per-channel or per-token,
+ * values per-token); a code maps back to code * scale + zero, taken as one
+ * fused multiply-add (the pages give no dequantization formula; one
+ * rounding makes this call exact and reproducible). Paged mode (pages != NULL; seq_lens ignored) lists each
  * request's INT2 tokens first, then its INT4 tokens.
  *   Errors: INVALID_ARG, CAPACITY, HIP.
  */

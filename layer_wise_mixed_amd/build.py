@@ -34,21 +34,28 @@ def compile_flags() -> list[str]:
             "-fno-fast-math", "-Wall", "-Wno-unused-function"]
 
 
+def _compile(cc: str, src: str, verbose: bool) -> str:
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = [cc] + compile_flags() + (["-x", "hip"] if src.endswith(".hip") else []) + ["-c", path, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    return obj
+
+
 def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel, one hipcc process each) and link libkvq.so."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = []
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(BUILD, src + ".o")
-        cmd = [cc] + compile_flags() + (["-x", "hip"] if src.endswith(".hip") else []) + ["-c", path, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError(f"hipcc failed on {src}")
-        objs.append(obj)
+    from concurrent.futures import ThreadPoolExecutor
+
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(cc, s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -51,7 +51,7 @@ struct Timer {
 } g_timer;
 
 void timer_free_locked() {
-  for (int k = 0; k < 3; ++k)
+  for (int k = 0; k < kTimerKinds; ++k)
     for (int i = 0; i < 2; ++i) {
       for (hipEvent_t e : g_timer.ev[k][i]) (void)hipEventDestroy(e);
       g_timer.ev[k][i].clear();
@@ -63,7 +63,6 @@ void timer_free_locked() {
 
 // Event pair for the next launch of `kind` if the timer is armed and has room.
 bool timer_slot(int kind, kvq::EventPair* ev) {
-  if (!g_timer.armed) return false;
   std::lock_guard<std::mutex> lk(g_timer.mu);
   if (!g_timer.armed || g_timer.used[kind] >= g_timer.capacity) return false;
   const int slot = g_timer.used[kind]++;
@@ -123,6 +122,7 @@ kvq::PagedGeom paged_geom(const kvq_plan* plan, int32_t layer, const kvq_pages* 
   pg.int2_add = pages->int2_add;
   pg.max_pages = pages->max_pages_per_req;
   pg.int2_pages = plan->shape.int2_pages;
+  pg.int4_pages = plan->shape.int4_pages;
   pg.int4_offset = lp.int4_offset;
   pg.int2_page_bytes = lp.int2_page_bytes;
   pg.int4_page_bytes = lp.int4_page_bytes;

@@ -167,7 +167,9 @@ __global__ __launch_bounds__(256) void paged_append_kernel(AppendArgs a) {
       xs[1][i][c] = vn[(size_t)(GS * x + i) * D + c];
     }
     __syncthreads();
-    const int pair = table[(n2_old + GS * x) / PAGE_TOKENS];
+    const int entry = (n2_old + GS * x) / PAGE_TOKENS;
+    const int pair = entry + 1 < pg.max_pages ? table[entry] : -1;
+    if (!int2_pair_ok(pg, entry, pair)) return;  // a bad table entry: nothing is written
     uint8_t* rec = g.base + (size_t)pair * pg.int2_page_bytes + (size_t)h * INT2_RECORD;
     quantize_record(xs, cs, rec, 2, 2, 0, tid);
     return;
@@ -179,7 +181,9 @@ __global__ __launch_bounds__(256) void paged_append_kernel(AppendArgs a) {
   const int t_lo = max(n4_old, PAGE_TOKENS * P), t_hi = min(n4_old + n4_add, PAGE_TOKENS * (P + 1));
   if (t_lo >= t_hi) return;
   const int p_lo = t_lo - PAGE_TOKENS * P, p_hi = t_hi - PAGE_TOKENS * P;  // slots written
-  const int id = table[(n2_old + add2) / PAGE_TOKENS + P];
+  const int entry = (n2_old + add2) / PAGE_TOKENS + P;
+  const int id = entry < pg.max_pages ? table[entry] : -1;
+  if (!int4_page_ok(pg, entry, id)) return;  // a bad table entry: nothing is written
   uint8_t* page = g.base + pg.int4_offset + (size_t)(id - pg.int2_pages) * pg.int4_page_bytes + (size_t)h * INT4_HEAD;
   for (int idx = tid; idx < PAGE_TOKENS * D; idx += blockDim.x) {
     const int p = idx >> 7, c = idx & 127;

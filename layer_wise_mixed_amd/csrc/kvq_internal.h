@@ -137,6 +137,7 @@ struct PagedGeom {
   const int32_t* int2_add;  // append: [batch] or null (= 0)
   int max_pages;
   int int2_pages;
+  int int4_pages;
   uint64_t int4_offset;
   uint64_t int2_page_bytes;
   uint64_t int4_page_bytes;
@@ -152,6 +153,17 @@ struct LayerGeom {
   int hkv, hq, g;
   int max_tokens;
 };
+
+// Page ids a write may use (the kernels check them before writing, so a bad
+// table never sends a write outside the layer's pool): an INT2 pair needs an
+// even id P with P + 1 < int2_pages, an INT4 page an id in [int2_pages,
+// int2_pages + int4_pages), and both a table entry below max_pages.
+__device__ inline bool int2_pair_ok(const PagedGeom& pg, int entry, int id) {
+  return entry >= 0 && entry + 1 < pg.max_pages && id >= 0 && (id & 1) == 0 && id + 1 < pg.int2_pages;
+}
+__device__ inline bool int4_page_ok(const PagedGeom& pg, int entry, int id) {
+  return entry >= 0 && entry < pg.max_pages && id >= pg.int2_pages && id < pg.int2_pages + pg.int4_pages;
+}
 
 struct AppendArgs {
   LayerGeom geo;

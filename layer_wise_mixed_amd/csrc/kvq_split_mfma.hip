@@ -951,7 +951,8 @@ __device__ __forceinline__ void append_int4_token_wave(uint8_t* page, const uint
 
 template <int NS>
 __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<NS>& sm, int r, int h, int split,
-                                                 int g0, int g1, int n4, int n4_old, const int32_t* table) {
+                                                 int g0, int g1, int n4, int n4_old, const int32_t* table,
+                                                 int e4) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   Lane ln;
@@ -978,7 +979,11 @@ __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<
   // token goes in first; otherwise while the first group loads. The fence
   // completes the writes before the wave's later loads.
   const int pn = n4_old / GS;
-  const bool own = a.k_new != nullptr && pn >= g0 && pn < g1 && ((pn - g0) & (kWaves - 1)) == wave;
+  // (e4: the table entry of the request's first INT4 page; a page id the
+  // table gives for the new token must be an INT4 page, or nothing is written)
+  const int entry = e4 + n4_old / PAGE_TOKENS;
+  const bool own = a.k_new != nullptr && pn >= g0 && pn < g1 && ((pn - g0) & (kWaves - 1)) == wave &&
+                   entry < a.pg.max_pages && int4_page_ok(a.pg, entry, table[n4_old / PAGE_TOKENS]);
   const bool early = own && pn == first && pn < qend;
   auto append = [&] {
     const size_t sigma = (size_t)r * a.geo.hkv + h;
@@ -1050,7 +1055,7 @@ __global__ __launch_bounds__(256, 2) void paged_split_kernel(DecodeArgs a) {
     const int g0 = i < s4 ? i * gps : n4g;
     const int g1 = i < s4 - 1 ? g0 + gps : n4g;
     const int32_t* table4 = table + n2 / PAGE_TOKENS;
-    paged_int4_split<NS>(a, sm, r, h, split, g0, g1, n4, n4_old, table4);
+    paged_int4_split<NS>(a, sm, r, h, split, g0, g1, n4, n4_old, table4, n2 / PAGE_TOKENS);
   }
 }
 

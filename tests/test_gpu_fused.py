@@ -41,7 +41,11 @@ def _buffers(gpu, c, max_len, splits):
     return out, lse, ws
 
 
-@pytest.mark.parametrize("hq,hkv,splits", [(8, 2, 1), (8, 2, 3), (7, 1, 0)])
+# G = 4 with one split and several, then every GQA group size class the split pass
+# instantiates: 4 column slots (G <= 4), 2 slots (G 5..8, G = 8 filling all 16 columns) and
+# one slot (G 9..16)
+@pytest.mark.parametrize("hq,hkv,splits", [(8, 2, 1), (8, 2, 3), (7, 1, 0), (2, 1, 0), (6, 2, 2), (10, 2, 0),
+                                           (12, 2, 0), (16, 2, 3), (9, 1, 0), (24, 2, 0), (16, 1, 2)])
 def test_fused_equals_separate_calls_and_oracle(gpu, oq, hq, hkv, splits):
     a = Case(gpu, oq, hq=hq, hkv=hkv, batch=len(LENS0), cap=CAP, cfgs=CFGS, lens=LENS0, seed=11)
     b = Case(gpu, oq, hq=hq, hkv=hkv, batch=len(LENS0), cap=CAP, cfgs=CFGS, lens=LENS0, seed=11)
@@ -76,7 +80,7 @@ def test_fused_equals_separate_calls_and_oracle(gpu, oq, hq, hkv, splits):
             a.v[l] = syn.values_fp16(a.seed, l, range(a.batch), range(hkv), 0, max_len)
             q, oa, la = outs[l]
             ref, ref_lse = a.oracle_decode(l, q)
-            check_attention(oa, la, ref, ref_lse, after, hq)
+            check_attention(oa, la, ref, ref_lse, after, hq, hkv)
         lens = after
 
 

@@ -97,7 +97,25 @@ class Case:
         return out, lse
 
 
-def check_attention(out, lse, ref, ref_lse, lens, hq):
+def check_streams(out, ref, lens, hkv):
+    """rel L2 <= 1e-3 on every (request, KV head) block of G query rows on its own, so that one
+    bad stream cannot hide under the batch's aggregate (a tiny absolute floor of 1e-6 keeps
+    blocks whose reference is exactly zero meaningful)."""
+    G = out.shape[1] // hkv
+    for r, L in enumerate(lens):
+        if L == 0:
+            continue
+        for h in range(hkv):
+            o = out[r, h * G:(h + 1) * G].astype(np.float64)
+            rf = ref[r, h * G:(h + 1) * G]
+            err = np.linalg.norm(o - rf)
+            assert err <= REL_L2 * np.linalg.norm(rf) + 1e-6, \
+                f"request {r} KV head {h} (L={L}): rel L2 {err / max(np.linalg.norm(rf), 1e-30):.3g}"
+
+
+def check_attention(out, lse, ref, ref_lse, lens, hq, hkv=None):
+    """The batch-level bar (rel L2 <= 1e-3, max abs <= 2e-3, lse within 1e-4), and with hkv the
+    same rel L2 bar on every (request, KV head) stream."""
     empty = [r for r, L in enumerate(lens) if L == 0]
     full = [r for r, L in enumerate(lens) if L > 0]
     for r in empty:
@@ -108,6 +126,8 @@ def check_attention(out, lse, ref, ref_lse, lens, hq):
     assert rel <= REL_L2, f"rel L2 {rel:.3g}"
     assert mx <= MAX_ABS, f"max abs {mx:.3g}"
     assert np.abs(lse[full] - ref_lse[full]).max() <= LSE_ABS
+    if hkv is not None:
+        check_streams(out, ref, lens, hkv)
     return rel, mx
 
 
@@ -154,7 +174,7 @@ def test_decode_attention_parity(ragged, splits):
         q = syn.queries_fp16(c.seed, l, 0, c.batch, c.hq).cuda()
         out, lse = c.decode(l, q, splits)
         ref, ref_lse = c.oracle_decode(l, q)
-        check_attention(out, lse, ref, ref_lse, c.lens, c.hq)
+        check_attention(out, lse, ref, ref_lse, c.lens, c.hq, c.hkv)
 
 
 def test_decode_fp16_output(ragged):
@@ -163,7 +183,7 @@ def test_decode_fp16_output(ragged):
     q = syn.queries_fp16(c.seed, l, 1, c.batch, c.hq).cuda()
     out, lse = c.decode(l, q, 0, torch.float16)
     ref, ref_lse = c.oracle_decode(l, q)
-    check_attention(out, lse, ref, ref_lse, c.lens, c.hq)
+    check_attention(out, lse, ref, ref_lse, c.lens, c.hq, c.hkv)
 
 
 def test_decode_deterministic(ragged):
@@ -187,7 +207,7 @@ def test_every_tail_length(gpu, oq):
             out, lse = c.decode(l, q, splits)
             ref, ref_lse = c.oracle_decode(l, q)
             try:
-                check_attention(out, lse, ref, ref_lse, c.lens, c.hq)
+                check_attention(out, lse, ref, ref_lse, c.lens, c.hq, c.hkv)
             except AssertionError as e:
                 raise AssertionError(f"layer {l} {c.cfgs[l]} splits {splits}: {e}") from None
 
@@ -200,7 +220,7 @@ def test_gqa_shapes(gpu, oq, hq, hkv):
         q = syn.queries_fp16(5, l, 0, 2, hq).cuda()
         out, lse = c.decode(l, q)
         ref, ref_lse = c.oracle_decode(l, q)
-        check_attention(out, lse, ref, ref_lse, c.lens, hq)
+        check_attention(out, lse, ref, ref_lse, c.lens, hq, hkv)
 
 
 def test_incremental_appends_match_oracle(gpu, oq):
