@@ -578,6 +578,7 @@ def time_workload(wl, K, W, graph=True):
         merge_ms, merge_n = kvq.timer_read(kvq.TIMER_MERGE)
         app_ms, app_n = kvq.timer_read(kvq.TIMER_APPEND)
         kvq.timer_stop()
+    graph_used = graphs is not None
     del graphs
     positions = [i % wl.C for i in range(K)]
     bytes_total = sum(wl.split_bytes(p) for p in positions)
@@ -593,7 +594,7 @@ def time_workload(wl, K, W, graph=True):
             "merge_us": merge_ms * 1e3 / max(merge_n, 1), "merge_n": merge_n,
             "append_us": app_ms * 1e3 / max(app_n, 1), "append_n": app_n,
             "eff_gbs": bytes_total / (gpu_ms / 1e3) / 1e9,
-            "traffic": _traffic(wl.name, window), "graph": graphs is not None or graph}
+            "traffic": _traffic(wl.name, window), "graph": graph_used}
 
 
 def roofline_obj(m, fused):

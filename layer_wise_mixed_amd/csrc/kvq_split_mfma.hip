@@ -8,18 +8,22 @@
 // partial for the merge pass. Per group:
 //
 //  scores  S[token][col] = sum_ch A[token][ch] * B[ch][col]   (two 16x16x32 f16 MFMA tiles)
-//          A = the packed key codes, fed to the MFMA as fp16 denormals: the code
-//              bits sit at the top of the fp16 mantissa, so a b-bit code x is the
-//              exact value x * 2^(-14-b) (one shift and one mask per register);
-//          B = q' * scale_k (q' = q * softmax_scale * log2 e; per-channel keys),
-//              as an fp16 high part and a 2^11-scaled fp16 low part, each with
-//              its own accumulator, so the product keeps ~22 significant bits;
-//          score = S * 2^(14+b) + sum_ch q'_ch * zero_ch.
+//          A = the packed key codes, fed to the MFMA as fp16 denormals: a b-bit
+//              code x sits in the mantissa as the exact value x * 2^-u(b)
+//              (u = 16, 20, 24 for 2, 4, 8 bits; one mask, or a shift and a mask,
+//              or one byte permute per register);
+//          B = q'' * scale_k, q'' = q * softmax_scale * log2 e * 2^-E with a
+//              power of two per query row that brings max |q''| into [1/2, 1)
+//              (so |B| <= 43669 for any fp16 keys), as an fp16 high part and the
+//              fp16 rounding of what it missed (taken from the exact product),
+//              both into one accumulator: ~21 significant bits;
+//          score = S * 2^u * 2^E + sum_ch q'_ch * zero_ch.
 //  softmax exp2 of (score - running max), rescaled lazily when the max grows.
 //  output  O^T[ch][col] += sum_tok V[tok][ch] * Pt[tok][col]  (eight 16x16x32 MFMA tiles)
-//          V: the value codes as denormals again, Pt = p * scale_v (high and
-//          2^11-scaled low parts); the zero-point term sum_tok p * zero_v is
-//          kept on the side.
+//          V: the value codes as denormals again, Pt = p * scale_v (high part
+//          and a 2^10-scaled low part with its own accumulator, so that values
+//          of tiny groups keep their precision); the zero-point term sum_tok p *
+//          zero_v is kept on the side.
 //
 // Columns. The 16 columns of the 16x16 tiles carry (query row g of the GQA
 // group = col % G, slot = col / G). On the output side the slot is a 32-channel
@@ -52,32 +56,36 @@ constexpr int kWaves = 4;
 
 __device__ inline f4_t mfma(h8_t a, h8_t b, f4_t c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-// 2^(14+b): the value of code 1 as the MFMA sees it is 2^(-14-b).
+// 2^u(b): the value of code 1 as the MFMA sees it is 2^-u(b).
 template <int B>
 __device__ constexpr float code_scale() {
-  return B == 2 ? 65536.0f : B == 4 ? 262144.0f : B == 8 ? 4194304.0f : 1.0f;
+  return B == 2 ? 65536.0f : B == 4 ? 1048576.0f : B == 8 ? 16777216.0f : 1.0f;
 }
 
 // The 8 codes at positions 8u..8u+7 of a lane's sequence as an MFMA operand:
 // consecutive position pairs become the two fp16 halves of one register, each
-// code at mantissa bits 10-b .. 9 of an fp16 denormal. Keeping the code at the
-// top of the mantissa matters: the matrix cores add products of tiny
-// denormals with visibly less precision than the same products placed high.
+// code in the mantissa of an fp16 denormal: 8-bit codes at bits 0..7 (one
+// byte permute), 4-bit codes at bits 4..7, 2-bit codes at bits 8..9. Codes
+// of two or four bits are kept away from the bottom of the mantissa: the
+// matrix cores add products of the smallest denormals with less precision
+// (measured on gfx950 against exact sums: relative error ~1e-6 for 2- and
+// 4-bit codes at bits 0.., ~2e-8 at bits 4.. and 8.., ~7e-8 for 8-bit
+// codes at bits 0..).
 template <int B>
 __device__ inline h8_t unpack8(const uint32_t* w, int u) {
   u4_t r;
   if constexpr (B == 8) {
     const uint32_t x = w[2 * u], y = w[2 * u + 1];
-    r[0] = (x << 2) & 0x03FC03FCu;
-    r[1] = (x >> 6) & 0x03FC03FCu;
-    r[2] = (y << 2) & 0x03FC03FCu;
-    r[3] = (y >> 6) & 0x03FC03FCu;
+    r[0] = __builtin_amdgcn_perm(0u, x, 0x0c020c00u);  // bytes 0 and 2: positions 0 and 1
+    r[1] = __builtin_amdgcn_perm(0u, x, 0x0c030c01u);  // bytes 1 and 3: positions 2 and 3
+    r[2] = __builtin_amdgcn_perm(0u, y, 0x0c020c00u);
+    r[3] = __builtin_amdgcn_perm(0u, y, 0x0c030c01u);
   } else if constexpr (B == 4) {
     const uint32_t x = w[u];
-    r[0] = (x << 6) & 0x03C003C0u;
-    r[1] = (x << 2) & 0x03C003C0u;
-    r[2] = (x >> 2) & 0x03C003C0u;
-    r[3] = (x >> 6) & 0x03C003C0u;
+    r[0] = (x << 4) & 0x00F000F0u;
+    r[1] = x & 0x00F000F0u;
+    r[2] = (x >> 4) & 0x00F000F0u;
+    r[3] = (x >> 8) & 0x00F000F0u;
   } else if constexpr (B == 2) {
     const uint32_t x = w[u >> 1];
     if (u & 1) {
@@ -113,22 +121,38 @@ __device__ inline void load_codes(const uint8_t* blk, int lane, uint32_t* w) {
   }
 }
 
-// elements i, i+1 of (hi, lo): an fp16 rounding of x, and what it missed,
-// scaled by 2^11, rounded to fp16 (the low part stays in the normal fp16 range
-// whenever x does), so hi + lo / 2^11 keeps ~21 significant bits of x. The
-// high part is one packed round-toward-zero conversion, an operation the
-// compiler cannot re-form from the product behind x: were it to round the
-// product once in one place (a fused multiply-round) and twice in another, the
-// two parts would disagree by an fp16 ulp.
-constexpr float kLoUp = 2048.0f;
-constexpr float kLoDown = 1.0f / 2048.0f;
+// Value side, elements i, i+1 of (hi, lo): an fp16 rounding of x and what it
+// missed, scaled by 2^10 and rounded to fp16, so hi + lo / 2^10 keeps ~21
+// significant bits of x, also for the tiny x of tiny value groups. The high
+// part is one packed round-toward-zero conversion, an operation the compiler
+// cannot re-form from the product behind x (were it to round that product
+// once in one place and twice in another, the parts would disagree by an
+// ulp). Its residual is below one fp16 ulp of x, so the scaled low part stays
+// below |x| (x = p * scale_v <= (65504 + 65504) / 3 for fp16 values: no
+// overflow).
+constexpr float kLoUp = 1024.0f;
+constexpr float kLoDown = 1.0f / 1024.0f;
 
 __device__ inline void set_hi_lo2(h8_t& hi, h8_t& lo, int i, float x0, float x1) {
   const auto h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
   hi[i] = h[0];
   hi[i + 1] = h[1];
-  lo[i] = (_Float16)((x0 - (float)h[0]) * kLoUp);
-  lo[i + 1] = (_Float16)((x1 - (float)h[1]) * kLoUp);
+  lo[i] = (_Float16)fmaf(-(float)h[0], kLoUp, x0 * kLoUp);
+  lo[i + 1] = (_Float16)fmaf(-(float)h[1], kLoUp, x1 * kLoUp);
+}
+
+// Score side, elements i, i+1 of (hi, lo) for x = a * b: the packed
+// round-toward-zero fp16 of x, and the fp16 rounding of a * b - hi (the
+// compiler takes it from the exact product in one mixed-precision fma), both
+// multiplied into one accumulator. Scores need absolute, not relative,
+// accuracy, and the low part's absolute error is at most 2^-25 even where it
+// falls in the fp16 denormal range.
+__device__ inline void set_hi_lo2_prod(h8_t& hi, h8_t& lo, int i, float a0, float b0, float a1, float b1) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(a0 * b0, a1 * b1);
+  hi[i] = h[0];
+  hi[i + 1] = h[1];
+  lo[i] = (_Float16)(a0 * b0 - (float)h[0]);
+  lo[i + 1] = (_Float16)(a1 * b1 - (float)h[1]);
 }
 
 __device__ inline void wave_sync_lds() {
@@ -156,7 +180,8 @@ __device__ inline float bpermute(int addr, float v) {
 struct Lane {
   int lane, la, gcol, slot, g;
   bool col_ok;
-  const float* qv;  // LDS: q' of the lane's row at channels 32 s + 8 la + i is qv[32 s + i]
+  const float* qv;  // LDS: q'' = q' 2^-E of the lane's row at channels 32 s + 8 la + i is qv[32 s + i]
+  float qe;         // 2^E of the lane's row
   float qn[4];      // per 32-channel group sums of q' (per-token keys)
 };
 
@@ -165,29 +190,50 @@ struct Acc {
   float m, lpart, zpart[4];
 };
 
-// B operand of q' alone (keys without per-channel scale: fp16 tail, 16-bit
-// and per-token keys)
-__device__ inline void q_operands(const Lane& ln, h8_t* qh, h8_t* ql) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) set_hi_lo2(qh[s], ql[s], i, ln.qv[32 * s + i], ln.qv[32 * s + i + 1]);
+// The score B operand lives in the wave's own LDS, not in registers (it is
+// reused by up to four groups, and 32 registers held across the group loop
+// are what would spill): for K-step s, the high parts at bst[2s][lane] and
+// the low parts at bst[2s + 1][lane], one 16-byte piece per lane. Each lane
+// reads back only what it wrote, so program order is the only ordering
+// needed.
+typedef u4_t BStore[8][64];
+
+__device__ __forceinline__ void store_b(BStore& bst, int s, int lane, const h8_t& hi, const h8_t& lo) {
+  bst[2 * s][lane] = __builtin_bit_cast(u4_t, hi);
+  bst[2 * s + 1][lane] = __builtin_bit_cast(u4_t, lo);
 }
 
-// B operand q' * scale_k of per-channel keys for the group of this lane's slot,
-// and beta = sum over all 128 channels of q' * zero_k for the lane's column.
-__device__ inline float k_operands(const Lane& ln, const float* kmeta, h8_t* bh, h8_t* bl) {
+// B operand of q'' alone (keys without per-channel scale: fp16 tail, 16-bit
+// and per-token keys)
+__device__ inline void q_operands(const Lane& ln, BStore& bst) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    h8_t qh, ql;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2)
+      set_hi_lo2_prod(qh, ql, i, ln.qv[32 * s + i], 1.0f, ln.qv[32 * s + i + 1], 1.0f);
+    store_b(bst, s, ln.lane, qh, ql);
+  }
+}
+
+// B operand q'' * scale_k of per-channel keys for the group of this lane's
+// slot, and beta = sum over all 128 channels of q' * zero_k for the lane's
+// column.
+__device__ inline float k_operands(const Lane& ln, const float* kmeta, BStore& bst) {
   const float* ks = kmeta + 32 * ln.la;
   float beta = 0.f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < 4; ++s) {
+    h8_t bh, bl;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
       const float q0 = ln.qv[32 * s + i], q1 = ln.qv[32 * s + i + 1];
-      set_hi_lo2(bh[s], bl[s], i, q0 * ks[8 * s + i], q1 * ks[8 * s + i + 1]);
+      set_hi_lo2_prod(bh, bl, i, q0, ks[8 * s + i], q1, ks[8 * s + i + 1]);
       beta = fmaf(q1, ks[128 + 8 * s + i + 1], fmaf(q0, ks[128 + 8 * s + i], beta));
     }
-  return sum_lane_groups(beta);
+    store_b(bst, s, ln.lane, bh, bl);
+  }
+  return sum_lane_groups(beta) * ln.qe;
 }
 
 // Scores of one 32-token group in log2 units, token 16 t + 4 la + i at index
@@ -197,20 +243,21 @@ __device__ inline float k_operands(const Lane& ln, const float* kmeta, h8_t* bh,
 // over slots; < 0: its own); kmeta: LDS copy of the group's key meta
 // (per-token keys). Tail slots at or past ntok get -inf.
 template <int KB, bool KTOK, bool TAIL>
-__device__ __forceinline__ void group_scores(const uint32_t* kw, const float* kmeta, int ntok, const h8_t* bh,
-                                             const h8_t* bl, float beta, int src, const Lane& ln, float* sc) {
+__device__ __forceinline__ void group_scores(const uint32_t* kw, const float* kmeta, int ntok, const BStore& bst,
+                                             float beta, int src, const Lane& ln, float* sc) {
+  const float cs = code_scale<KB>() * ln.qe;
   if constexpr (!KTOK || KB == 16) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      f4_t c = {0.f, 0.f, 0.f, 0.f}, cl = {0.f, 0.f, 0.f, 0.f};
+      f4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const h8_t A = unpack8<KB>(kw, 4 * t + s);
-        c = mfma(A, bh[s], c);
-        cl = mfma(A, bl[s], cl);
+        c = mfma(A, __builtin_bit_cast(h8_t, bst[2 * s][ln.lane]), c);
+        c = mfma(A, __builtin_bit_cast(h8_t, bst[2 * s + 1][ln.lane]), c);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[4 * t + i] = fmaf(fmaf(cl[i], kLoDown, c[i]), code_scale<KB>(), beta);
+      for (int i = 0; i < 4; ++i) sc[4 * t + i] = fmaf(c[i], cs, beta);
     }
     if constexpr (KB < 16) {
       if (src >= 0) {
@@ -226,15 +273,14 @@ __device__ __forceinline__ void group_scores(const uint32_t* kw, const float* km
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        f4_t c = {0.f, 0.f, 0.f, 0.f}, cl = {0.f, 0.f, 0.f, 0.f};
+        f4_t c = {0.f, 0.f, 0.f, 0.f};
         const h8_t A = unpack8<KB>(kw, 4 * t + s);
-        c = mfma(A, bh[s], c);
-        cl = mfma(A, bl[s], cl);
+        c = mfma(A, __builtin_bit_cast(h8_t, bst[2 * s][ln.lane]), c);
+        c = mfma(A, __builtin_bit_cast(h8_t, bst[2 * s + 1][ln.lane]), c);
         const float* km = kmeta + 32 * s + 8 * ln.la + 4 * t;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          sc[4 * t + i] = fmaf(fmaf(cl[i], kLoDown, c[i]) * code_scale<KB>(), km[i],
-                               fmaf(km[128 + i], ln.qn[s], sc[4 * t + i]));
+          sc[4 * t + i] = fmaf(c[i] * cs, km[i], fmaf(km[128 + i], ln.qn[s], sc[4 * t + i]));
       }
     }
   }
@@ -335,10 +381,10 @@ __device__ __forceinline__ void group_pv(const uint32_t* vw, const float* vmeta,
 
 template <int KB, int VB, bool KTOK, int NS, bool TAIL, bool VPAGE = false>
 __device__ __forceinline__ void process_group(const uint32_t* kw, const uint32_t* vw, const float* kmeta,
-                                              const float* vmeta, int ntok, const h8_t* bh, const h8_t* bl,
+                                              const float* vmeta, int ntok, const BStore& bst,
                                               float beta, int src, const Lane& ln, Acc& acc) {
   float sc[8];
-  group_scores<KB, KTOK, TAIL>(kw, kmeta, ntok, bh, bl, beta, src, ln, sc);
+  group_scores<KB, KTOK, TAIL>(kw, kmeta, ntok, bst, beta, src, ln, sc);
   raise_max(fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))),
             acc);
   group_pv<VB, NS, TAIL, VPAGE>(vw, vmeta, ntok, sc, ln, acc);
@@ -362,9 +408,15 @@ struct alignas(16) SplitSmem {
     Loop loop;
     Flush flush;
   };
-  float o[kWaves][kMaxG][D];  // per wave: its result, for the combine
+  // per wave: the score B operand during its group loop, then its result
+  // for the combine (a wave writes its result once its own loop is done)
+  union WaveLds {
+    BStore b;
+    float o[kMaxG][D];
+  } wl[kWaves];
   float ml[kWaves][2][kMaxG];
-  float q[kMaxG][D];  // q' of the G query rows (every wave writes the same values)
+  float q[kMaxG][D];  // q'' of the G query rows (every wave writes the same values)
+  float qe[kMaxG];    // 2^E of each row
 };
 
 // The query rows of a workgroup, the G query heads of one KV head
@@ -380,8 +432,8 @@ struct HeadRows {
 // and (per-token keys) the sums of q' over each 32-channel group. Every wave
 // writes all of q' (the same values), so no wave waits for another.
 template <int NS, bool QN>
-__device__ __forceinline__ void setup_lane(const DecodeArgs& a, int G, const HeadRows& rows, float (*s_q)[D], Lane& ln,
-                                           Acc& acc) {
+__device__ __forceinline__ void setup_lane(const DecodeArgs& a, int G, const HeadRows& rows, float (*s_q)[D],
+                                           float* s_qe, Lane& ln, Acc& acc) {
   const int tid = threadIdx.x;
   ln.lane = tid & 63;
   ln.la = ln.lane >> 4;
@@ -390,28 +442,42 @@ __device__ __forceinline__ void setup_lane(const DecodeArgs& a, int G, const Hea
   ln.gcol = c16 % G;
   ln.slot = c16 / G;
   ln.col_ok = ln.slot < NS;
-  for (int c = ln.lane; c < G * (D / 8); c += 64) {  // 8 values a lane at a time
+  // 8 values a lane at a time: in each pass the 16 lanes 16k .. 16k + 15 hold
+  // one whole row, so the row's largest |q'| is a max over those 16 lanes
+  for (int c = ln.lane; c < G * (D / 8); c += 64) {
     const u4_t w = *(const u4_t*)(rows.ptr(0) + 8 * c);
     const h8_t x = __builtin_bit_cast(h8_t, w);
+    float v[8], mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = (float)x[i] * a.scale_log2;
+      mx = fmaxf(mx, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+    int E = 0;
+    (void)frexpf(mx, &E);  // max |q'| = f 2^E, f in [1/2, 1); E = 0 for a zero row
     float* dst = &s_q[c >> 4][8 * (c & 15)];
     f4_t lo4, hi4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      lo4[i] = (float)x[i] * a.scale_log2;
-      hi4[i] = (float)x[4 + i] * a.scale_log2;
+      lo4[i] = ldexpf(v[i], -E);
+      hi4[i] = ldexpf(v[4 + i], -E);
     }
     *(f4_t*)dst = lo4;
     *(f4_t*)(dst + 4) = hi4;
+    if ((c & 15) == 0) s_qe[c >> 4] = ldexpf(1.0f, E);
   }
   wave_sync_lds();
   ln.qv = &s_q[ln.gcol][8 * ln.la];
+  ln.qe = s_qe[ln.gcol];
   if constexpr (QN) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       float part = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) part += ln.qv[32 * s + i];
-      ln.qn[s] = sum_lane_groups(part);
+      ln.qn[s] = sum_lane_groups(part) * ln.qe;
     }
   }
 #pragma unroll
@@ -459,7 +525,7 @@ __device__ __forceinline__ void finish(const DecodeArgs& a, const HeadRows& rows
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          sm.o[wave][ln.gcol][32 * n + 16 * t + 4 * ln.la + i] = fmaf(fmaf(ol[t][i], kLoDown, o[t][i]), vmul, z);
+          sm.wl[wave].o[ln.gcol][32 * n + 16 * t + 4 * ln.la + i] = fmaf(fmaf(ol[t][i], kLoDown, o[t][i]), vmul, z);
     }
   }
   if (ln.lane < G) {
@@ -479,7 +545,7 @@ __device__ __forceinline__ void finish(const DecodeArgs& a, const HeadRows& rows
         const float mw = sm.ml[w][0][gg];
         if (mw == -INFINITY) continue;
         const float e = __builtin_amdgcn_exp2f(mw - M);
-        num = fmaf(e, sm.o[w][gg][c], num);
+        num = fmaf(e, sm.wl[w].o[gg][c], num);
         den = fmaf(e, sm.ml[w][1][gg], den);
       }
     }
@@ -591,8 +657,8 @@ __device__ __forceinline__ void progress_priority(int done, int nk) {
 // static (no register copies). setup() (the wave's q' setup) runs once the
 // first group's loads are issued, so that the two memory waits overlap.
 template <int KB, int VB, bool KTOK, int NS, int R, class Src, class Setup>
-__device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta, float* vmeta, const Lane& ln,
-                                           Acc& acc, Setup&& setup) {
+__device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta, float* vmeta, BStore& bst,
+                                           const Lane& ln, Acc& acc, Setup&& setup) {
   constexpr bool STACK = KB < 16 && !KTOK;  // per-channel keys: one B operand for R groups
   constexpr int NKW = 2 * KB, NVW = 2 * VB;
   constexpr bool VPAGE = Src::kVPage;
@@ -614,9 +680,8 @@ __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta,
   setup();
   if (nk <= 0) return;
   progress_priority(0, nk);
-  h8_t bh[4], bl[4];
   float beta = 0.f;
-  if constexpr (!STACK) q_operands(ln, bh, bl);
+  if constexpr (!STACK) q_operands(ln, bst);
   auto step = [&](auto J, int k) {
     constexpr int j = decltype(J)::value;
     const int e = STACK ? k % R : 0;  // slot of this group in its stack
@@ -637,10 +702,10 @@ __device__ __forceinline__ void run_groups(const Src& src, int nk, float* kmeta,
     }
     int srcl = -1;  // the lane holding this lane's scores: same row, column of slot e
     if constexpr (STACK) {
-      if (e == 0) beta = k_operands(ln, kmeta + 256 * (ln.col_ok ? ln.slot : 0), bh, bl);
+      if (e == 0) beta = k_operands(ln, kmeta + 256 * (ln.col_ok ? ln.slot : 0), bst);
       srcl = ((ln.lane & 48) | (ln.gcol + ln.g * e)) * 4;
     }
-    process_group<KB, VB, KTOK, NS, false, VPAGE>(buf[j].kw, buf[j].vw, kmeta, vmeta, GS, bh, bl, beta, srcl, ln,
+    process_group<KB, VB, KTOK, NS, false, VPAGE>(buf[j].kw, buf[j].vw, kmeta, vmeta, GS, bst, beta, srcl, ln,
                                                   acc);
     wave_sync_lds();
     progress_priority(k + 1, nk);
@@ -764,7 +829,8 @@ __device__ __forceinline__ void load_tail(const uint8_t* rec, int T, int lane, u
 
 template <int VB, int NS>
 __device__ __forceinline__ void tail_pass(uint8_t* rec, int T, const uint16_t* kn, const uint16_t* vn, uint32_t* kw,
-                                          uint32_t* vw, float* kmeta, float* vmeta, const Lane& ln, Acc& acc) {
+                                          uint32_t* vw, float* kmeta, float* vmeta, BStore& bst, const Lane& ln,
+                                          Acc& acc) {
   const int lane = ln.lane;
   if (kn) merge_new_token(rec, kn, vn, T - 1, lane, kw, vw);
   if constexpr (VB < 16) {
@@ -774,9 +840,8 @@ __device__ __forceinline__ void tail_pass(uint8_t* rec, int T, const uint16_t* k
       acc.ol[u] *= code_scale<VB>();
     }
   }
-  h8_t th[4], tl[4];
-  q_operands(ln, th, tl);
-  process_group<16, 16, false, NS, true>(kw, vw, kmeta, vmeta, T, th, tl, 0.f, -1, ln, acc);
+  q_operands(ln, bst);
+  process_group<16, 16, false, NS, true>(kw, vw, kmeta, vmeta, T, bst, 0.f, -1, ln, acc);
   if constexpr (VB < 16) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -851,14 +916,14 @@ __global__ __launch_bounds__(256, 2) void split_mfma_kernel(DecodeArgs a) {
   uint32_t tkw[32], tvw[32];
   if (own_tail && nk == 0) {
     load_tail(tail, T, threadIdx.x & 63, tkw, tvw);
-    setup_lane<NS, KTOK && KB < 16>(a, g.g, rows, sm.q, ln, acc);
-    tail_pass<VB, NS>(tail, T, kn, vn, tkw, tvw, kmeta, vmeta, ln, acc);
+    setup_lane<NS, KTOK && KB < 16>(a, g.g, rows, sm.q, sm.qe, ln, acc);
+    tail_pass<VB, NS>(tail, T, kn, vn, tkw, tvw, kmeta, vmeta, sm.wl[wave].b, ln, acc);
   } else {
-    run_groups<KB, VB, KTOK, NS, R>(src, nk, kmeta, vmeta, ln, acc,
-                                    [&] { setup_lane<NS, KTOK && KB < 16>(a, g.g, rows, sm.q, ln, acc); });
+    run_groups<KB, VB, KTOK, NS, R>(src, nk, kmeta, vmeta, sm.wl[wave].b, ln, acc,
+                                    [&] { setup_lane<NS, KTOK && KB < 16>(a, g.g, rows, sm.q, sm.qe, ln, acc); });
     if (own_tail) {
       load_tail(tail, T, threadIdx.x & 63, tkw, tvw);
-      tail_pass<VB, NS>(tail, T, kn, vn, tkw, tvw, kmeta, vmeta, ln, acc);
+      tail_pass<VB, NS>(tail, T, kn, vn, tkw, tvw, kmeta, vmeta, sm.wl[wave].b, ln, acc);
     }
   }
   finish<VB, NS>(a, rows, split, wave, sm, ln, acc);
@@ -882,8 +947,8 @@ __device__ __forceinline__ void paged_int2_split(const DecodeArgs& a, SplitSmem<
   src.page_bytes = a.pg.int2_page_bytes;
   src.ids = lane < nk ? table[2 * (first + kWaves * lane)] : 0;
   const HeadRows rows{a.q, (size_t)r * a.geo.hq + h * a.geo.g};
-  run_groups<2, 2, false, NS, NS>(src, nk, &sm.loop.kmeta[wave][0][0], sm.loop.vmeta[wave], ln, acc,
-                                  [&] { setup_lane<NS, false>(a, a.geo.g, rows, sm.q, ln, acc); });
+  run_groups<2, 2, false, NS, NS>(src, nk, &sm.loop.kmeta[wave][0][0], sm.loop.vmeta[wave], sm.wl[wave].b, ln, acc,
+                                  [&] { setup_lane<NS, false>(a, a.geo.g, rows, sm.q, sm.qe, ln, acc); });
   finish<2, NS>(a, rows, split, wave, sm, ln, acc);
 }
 
@@ -995,8 +1060,8 @@ __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   };
   if (early) append();
-  run_groups<4, 4, true, NS, 1>(src, nk, kmeta, vmeta, ln, acc, [&] {
-    setup_lane<NS, true>(a, a.geo.g, rows, sm.q, ln, acc);
+  run_groups<4, 4, true, NS, 1>(src, nk, kmeta, vmeta, sm.wl[wave].b, ln, acc, [&] {
+    setup_lane<NS, true>(a, a.geo.g, rows, sm.q, sm.qe, ln, acc);
     if (own && !early) append();
   });
 
@@ -1023,9 +1088,8 @@ __device__ __forceinline__ void paged_int4_split(const DecodeArgs& a, SplitSmem<
     *(u4_t*)(kmeta + 4 * lane) = km;
     *(u4_t*)(vmeta + 4 * lane) = vm;
     wave_sync_lds();
-    h8_t bh[4], bl[4];
-    q_operands(ln, bh, bl);
-    process_group<4, 4, true, NS, true, true>(kw, vw, kmeta, vmeta, ntok, bh, bl, 0.f, -1, ln, acc);
+    q_operands(ln, sm.wl[wave].b);
+    process_group<4, 4, true, NS, true, true>(kw, vw, kmeta, vmeta, ntok, sm.wl[wave].b, 0.f, -1, ln, acc);
     wave_sync_lds();
   }
   finish<4, NS>(a, rows, split, wave, sm, ln, acc);

@@ -108,17 +108,30 @@ class ExplicitCase:
                 kd, vd = self.oq.dequant_stream(sq)
                 o, ls = self.oq.attention(qq, kd, vd, SCALE)
                 ref[r, h * G:(h + 1) * G], ref_lse[r, h * G:(h + 1) * G] = o, ls
-                tol[r, h * G:(h + 1) * G] = lse_tolerance(qq, kd, SCALE)
+                tol[r, h * G:(h + 1) * G] = lse_tolerance(qq, kd, SCALE, kb, ax == 1)
         where = f"layer {l} {self.cfgs[l]} splits {splits}"
         for r, L in enumerate(self.lens):
             if L == 0:
                 assert np.all(out[r] == 0) and np.all(lse[r] == -np.inf), where
         full = [r for r, L in enumerate(self.lens) if L > 0]
         assert np.isfinite(out[full]).all(), f"{where}: non-finite output"
-        mx = np.abs(out[full] - ref[full]).max()
-        assert mx <= MAX_ABS, f"{where}: max abs {mx:.3g}"
+        # max abs 2e-3 on streams whose outputs are of unit scale; a stream whose reference
+        # output reaches beyond 1 in magnitude (values of |x| ~ 6e4) is held to 2e-3 times
+        # that magnitude: fp32 arithmetic carries relative, not absolute, error
+        for r in full:
+            for h in range(self.hkv):
+                blk = slice(h * G, (h + 1) * G)
+                scale = max(1.0, float(np.abs(ref[r, blk]).max()))
+                err = float(np.abs(out[r, blk] - ref[r, blk]).max())
+                assert err <= MAX_ABS * scale, \
+                    f"{where}: request {r} KV head {h}: max abs {err:.3g} (output scale {scale:.3g})"
         dl = np.abs(lse[full] - ref_lse[full])
-        assert (dl <= tol[full]).all(), f"{where}: lse off by {dl.max():.3g} (bound {tol[full].min():.3g})"
+        bad = np.argwhere(dl > tol[full])
+        if bad.size:
+            i, row = bad[0]
+            r = full[i]
+            raise AssertionError(f"{where}: request {r} row {row}: lse {lse[r, row]:.7g} vs {ref_lse[r, row]:.7g}, "
+                                 f"off by {dl[i, row]:.3g} (bound {tol[r, row]:.3g}); {len(bad)} rows over")
         try:
             check_streams(out, ref, self.lens, self.hkv)
         except AssertionError as e:
@@ -148,7 +161,9 @@ def edge_streams(seed, hkv, L):
     k[2, :, :, 5] = (rng.uniform(-3e4, 3e4, size=(hkv, L))).astype(np.float16)
     k[2, :, :, 100] = (rng.uniform(-3e4, 3e4, size=(hkv, L))).astype(np.float16)
     big = rng.choice(L, size=min(L, 4), replace=False)
-    v[3, :, big, :] = (rng.uniform(-6e4, 6e4, size=(hkv, len(big), 128))).astype(np.float16)
+    for h in range(hkv):
+        for j in big:
+            v[3, h, j, :] = rng.uniform(-6e4, 6e4, size=128).astype(np.float16)
     k[4] = (0.01 + rng.uniform(-5e-5, 5e-5, size=k[4].shape)).astype(np.float16)
     v[4] = (0.01 + rng.uniform(-5e-5, 5e-5, size=v[4].shape)).astype(np.float16)
     k[5] = rng.uniform(-5e-7, 5e-7, size=k[5].shape).astype(np.float16)

@@ -19,13 +19,34 @@ MAX_ABS = 2e-3
 LSE_ABS = 1e-4
 
 
-def lse_tolerance(q_fp16, kdeq, scale):
-    """Per-row bound on |lse - lse_oracle|: 1e-4 plus 2^-19 times the largest sum of absolute
-    products max_j sum_c |q_c k_jc| * scale. The split pass forms scores in fp32 from ~22-bit
-    products, and folding per-channel scales and zero points cancels terms of that size, so
-    its score error is a small multiple of 2^-22 of that sum; 2^-19 leaves a factor 8."""
+def fold_magnitude(kdeq, kb, k_token):
+    """Per (token, channel): the size of the terms the split pass adds in fp32 for that key
+    element. It forms a score from the folded quantizer, scale * (q . codes) plus zero * sum(q),
+    so a key element contributes |scale * code| + |zero| <= |k| + 2 |zero| (zero = the group's
+    minimum, which code 0 dequantizes to exactly); fp16 tail tokens and 16-bit layers contribute
+    |k|."""
+    k = np.asarray(kdeq, dtype=np.float64).reshape(-1, 128)
+    m = np.abs(k)
+    lq = (k.shape[0] // 32) * 32
+    if kb < 16 and lq:
+        g = k[:lq].reshape(lq // 32, 32, 128)
+        if k_token:  # a group is 32 channels of one token
+            zero = k[:lq].reshape(lq, 4, 32).min(axis=2)
+            m[:lq] += 2 * np.abs(np.repeat(zero, 32, axis=1))
+        else:  # a group is 32 tokens of one channel
+            zero = g.min(axis=1)
+            m[:lq] += 2 * np.abs(np.repeat(zero, 32, axis=0))
+    return m
+
+
+def lse_tolerance(q_fp16, kdeq, scale, kb=16, k_token=False):
+    """Per-row bound on |lse - lse_oracle|: 1e-4 plus 2^-19 times the largest sum over the
+    channels of |q_c| times the fold magnitude of key element (j, c), times scale. The split pass
+    forms scores in fp32 from ~22-bit products, and folding scales and zero points cancels terms
+    of the fold magnitude's size, so its score error is a small multiple of 2^-22 of that sum;
+    2^-19 leaves a factor 8."""
     q = np.abs(np.asarray(q_fp16, dtype=np.float64).reshape(-1, 128))
-    k = np.abs(np.asarray(kdeq, dtype=np.float64).reshape(-1, 128))
+    k = fold_magnitude(kdeq, kb, k_token)
     if k.shape[0] == 0:
         return np.full(q.shape[0], LSE_ABS)
     return LSE_ABS + 2.0 ** -19 * (q @ k.T).max(axis=1) * scale
