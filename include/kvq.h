@@ -230,6 +230,26 @@ int kvq_decode_attention(const kvq_plan *plan, int32_t layer, const void *cache,
                          int32_t num_splits, const kvq_pages *pages, kvq_stream_t stream);
 
 /*
+ * kvq_decode_attention_noalloc -- kvq_decode_attention for callers that
+ * cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid allocation): the same result, from the same
+ * kernels, with the split partials kept in a 16 MiB array of device memory
+ * that the library holds (one per GPU, until the process ends) instead of a
+ * caller-given workspace. It allocates nothing. Calls that overlap on one GPU
+ * (running at the same time on different streams) share that array and race.
+ *   Arguments as in kvq_decode_attention, without workspace and
+ *   workspace_bytes.
+ *   Errors: those of kvq_decode_attention, and WORKSPACE when the partials
+ *   (kvq_decode_workspace_bytes(plan, batch, max_seq_len, num_splits)) would
+ *   need more than 16 MiB.
+ */
+int kvq_decode_attention_noalloc(const kvq_plan *plan, int32_t layer, const void *cache,
+                                 const uint16_t *q, const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_seq_len, float softmax_scale, void *out,
+                                 int32_t out_dtype, float *lse_out, int32_t num_splits,
+                                 const kvq_pages *pages, kvq_stream_t stream);
+
+/*
  * kvq_append_decode_attention -- one decode step of one layer with its token
  * append fused in: the same result, in the cache and in out/lse_out, as
  * kvq_quantize_append with n_new = 1 followed by kvq_decode_attention with

@@ -71,7 +71,7 @@ class Pages(ctypes.Structure):
 
 
 SYMBOLS = ["kvq_plan_layers", "kvq_quantize_append", "kvq_decode_workspace_bytes", "kvq_decode_num_splits",
-           "kvq_decode_attention", "kvq_append_decode_attention", "kvq_prefix_workspace_bytes",
+           "kvq_decode_attention", "kvq_decode_attention_noalloc", "kvq_append_decode_attention", "kvq_prefix_workspace_bytes",
            "kvq_prefix_attention", "kvq_dequantize", "kvq_last_error", "kvq_timer_start", "kvq_timer_read",
            "kvq_timer_stop"]
 
@@ -99,6 +99,9 @@ def load():
     L.kvq_decode_attention.argtypes = [ctypes.POINTER(Plan), i32, P, P, P, i32, i32, ctypes.c_float, P, i32, P, P,
                                        ctypes.c_size_t, i32, ctypes.POINTER(Pages), P]
     L.kvq_decode_attention.restype = ctypes.c_int
+    L.kvq_decode_attention_noalloc.argtypes = [ctypes.POINTER(Plan), i32, P, P, P, i32, i32, ctypes.c_float, P, i32,
+                                               P, i32, ctypes.POINTER(Pages), P]
+    L.kvq_decode_attention_noalloc.restype = ctypes.c_int
     L.kvq_append_decode_attention.argtypes = [ctypes.POINTER(Plan), i32, P, P, P, P, P, i32, i32, ctypes.c_float,
                                               P, i32, P, P, ctypes.c_size_t, i32, ctypes.POINTER(Pages), P]
     L.kvq_append_decode_attention.restype = ctypes.c_int
@@ -207,6 +210,24 @@ def decode_attention(plan: Plan, layer: int, cache, q, seq_lens, max_seq_len: in
                                        OUT_F32 if out.dtype == torch.float32 else OUT_F16, _ptr(lse),
                                        _ptr(workspace), ws_bytes, num_splits,
                                        None if pages is None else ctypes.byref(pages), _stream(stream)))
+
+
+def decode_attention_noalloc(plan: Plan, layer: int, cache, q, seq_lens, max_seq_len: int, softmax_scale: float,
+                             out, lse=None, num_splits: int = 0, pages: Pages | None = None, stream=None):
+    """decode_attention with the split partials in the library's own device array (no workspace;
+    the library allocates nothing)."""
+    import torch
+
+    assert q.dtype == torch.float16 and q.is_contiguous()
+    assert out.is_contiguous() and out.dtype in (torch.float16, torch.float32)
+    batch = q.shape[0]
+    if seq_lens is not None:
+        _dev_i32(seq_lens, batch, "seq_lens")
+    _check(load().kvq_decode_attention_noalloc(ctypes.byref(plan), layer, _ptr(cache), _ptr(q), _ptr(seq_lens), batch,
+                                               max_seq_len, float(softmax_scale), _ptr(out),
+                                               OUT_F32 if out.dtype == torch.float32 else OUT_F16, _ptr(lse),
+                                               num_splits, None if pages is None else ctypes.byref(pages),
+                                               _stream(stream)))
 
 
 def append_decode_attention(plan: Plan, layer: int, cache, k_new, v_new, q, seq_lens, max_seq_len: int,

@@ -221,6 +221,11 @@ int32_t prefix_splits(const kvq_plan* plan, int32_t batch, int32_t chunk, int32_
 
 }  // namespace
 
+int kvq::set_error(int code, const char* msg) {
+  g_error = msg;
+  return code;
+}
+
 extern "C" {
 
 const char* kvq_last_error(void) { return g_error.c_str(); }

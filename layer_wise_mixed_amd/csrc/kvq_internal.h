@@ -232,6 +232,10 @@ hipError_t launch_append_paged(const AppendArgs& a, int batch, hipStream_t s, co
 hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s, const EventPair* ev);
 
+// Record the message kvq_last_error() returns on this thread, and return code
+// (for entry points defined outside kvq_api.cpp).
+int set_error(int code, const char* msg);
+
 // kernel launch with optional dispatch-bound events
 template <typename K, typename A>
 inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, const EventPair* ev, const A& args) {
