@@ -164,3 +164,18 @@ def seeded_bits(seed: int, tensor: int, request: int, n: int, device="cpu") -> t
 def seeded_permutation(seed: int, tensor: int, n: int, salt: int = 0) -> list[int]:
     key = stream_key(seed, tensor, salt, 1, 0)
     return sorted(range(n), key=lambda i: (fmix32_int(key ^ fmix32_int(i + GOLDEN)), i))
+
+
+def seeded_tags(seed: int, request: int, length: int, num_tags: int, mean_run: int = 48) -> list[int]:
+    """A seeded tag per token of one request (arrival order): runs of one tag, each run's length
+    uniform in [1, 2 mean_run - 1] and its tag uniform in [0, num_tags). Stands in for the role
+    tags of a chat's spans (system prompt, tool output, user turn, ...); no dataset is used."""
+    key = stream_key(seed, T_TAG, 0, request, 1)
+    out, i = [], 0
+    while len(out) < length:
+        h = fmix32_int(key ^ fmix32_int((i + GOLDEN) & MASK32))
+        run = 1 + h % (2 * mean_run - 1)
+        tag = (h >> 16) % num_tags
+        out.extend([tag] * run)
+        i += 1
+    return out[:length]
