@@ -320,6 +320,45 @@ int kvq_prefix_attention(const kvq_plan *plan, int32_t layer, const void *cache,
                          float *lse_out, void *workspace, size_t workspace_bytes,
                          int32_t num_splits, kvq_stream_t stream);
 
+/* Workspace bytes kvq_chunk_prefill_attention needs: batch * chunk * Hq *
+ * (splits + 1) * (128 + 1) fp32 (the prefix splits' partials and the chunk's
+ * own). num_splits = 0 means the count the library would choose. Returns 0 on
+ * invalid arguments. */
+size_t kvq_chunk_prefill_workspace_bytes(const kvq_plan *plan, int32_t batch, int32_t chunk,
+                                         int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * kvq_chunk_prefill_attention -- the whole attention of a prefill chunk that
+ * follows a quantized cache: every query row (chunk token i, query head)
+ * attends to the request's cached prefix as stored (packed groups and fp16
+ * tail, no mask) and, causally, to the chunk's own fp16 tokens 0 .. i (the
+ * chunk is quantized only when kvq_quantize_append later stores it). Three
+ * launches: the prefix pass of kvq_prefix_attention, a causal pass over the
+ * chunk's keys and values (matrix cores, fp16 operands), and the log-sum-exp
+ * merge of the prefix splits and the chunk part (TriAxialKV page, "Facts":
+ * partial attentions merged by online log-sum-exp). The result is softmax
+ * attention over the union, one softmax.
+ *   q: device fp16 [batch][chunk][Hq][128];
+ *   k_chunk, v_chunk: device fp16 [batch][Hkv][chunk][128], the chunk's own
+ *     keys and values;
+ *   seq_lens, max_seq_len, softmax_scale: as in kvq_prefix_attention (a
+ *     request with an empty prefix attends to its chunk only);
+ *   out: device fp32 [batch][chunk][Hq][128]; lse_out: device fp32
+ *     [batch][chunk][Hq], nullable;
+ *   workspace: kvq_chunk_prefill_workspace_bytes(...) bytes (never 0 for a
+ *     non-empty chunk); num_splits: 0 = automatic, else 1..1023 (prefix
+ *     splits);
+ *   cache, q, k_chunk, v_chunk, out and workspace 16-byte aligned.
+ * Contiguous plans only.
+ *   Errors: INVALID_ARG, UNSUPPORTED (paged plan), CAPACITY, WORKSPACE, HIP.
+ */
+int kvq_chunk_prefill_attention(const kvq_plan *plan, int32_t layer, const void *cache,
+                                const uint16_t *q, const uint16_t *k_chunk,
+                                const uint16_t *v_chunk, int32_t chunk, const int32_t *seq_lens,
+                                int32_t batch, int32_t max_seq_len, float softmax_scale,
+                                float *out, float *lse_out, void *workspace,
+                                size_t workspace_bytes, int32_t num_splits, kvq_stream_t stream);
+
 /*
  * kvq_dequantize -- the cache of one layer back in fp32, for checking:
  * k_out, v_out: device fp32 [batch][Hkv][max_seq_len][128]; token j of

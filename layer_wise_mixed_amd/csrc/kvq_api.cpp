@@ -547,6 +547,83 @@ int kvq_prefix_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   return hip_status(e, "merge launch");
 }
 
+size_t kvq_chunk_prefill_workspace_bytes(const kvq_plan* plan, int32_t batch, int32_t chunk, int32_t max_seq_len,
+                                         int32_t num_splits) {
+  if (!plan || batch < 0 || chunk < 0 || max_seq_len < 0 || num_splits < 0 || num_splits > 1024) return 0;
+  const int32_t s = num_splits ? num_splits : prefix_splits(plan, batch, chunk, max_seq_len);
+  return (size_t)batch * chunk * plan->shape.num_q_heads * (s + 1) * (kvq::D + 1) * sizeof(float);
+}
+
+int kvq_chunk_prefill_attention(const kvq_plan* plan, int32_t layer, const void* cache, const uint16_t* q,
+                                const uint16_t* k_chunk, const uint16_t* v_chunk, int32_t chunk,
+                                const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float softmax_scale,
+                                float* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                                int32_t num_splits, kvq_stream_t stream) {
+  int st = check_plan_layer(plan, layer);
+  if (st) return st;
+  if (is_paged(plan)) return fail(KVQ_ERR_UNSUPPORTED, "chunked prefill reads contiguous streams only");
+  if (!cache || !q || !k_chunk || !v_chunk || !out || !seq_lens)
+    return fail(KVQ_ERR_INVALID_ARG, "null cache, q, k_chunk, v_chunk, seq_lens or out");
+  if (!aligned16(cache) || !aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out) ||
+      !aligned16(workspace))
+    return fail(KVQ_ERR_INVALID_ARG, "cache, q, k_chunk, v_chunk, out and workspace must be 16-byte aligned");
+  if (batch < 0 || batch > plan->shape.max_batch)
+    return fail(KVQ_ERR_INVALID_ARG, "batch %d out of range [0, %d]", batch, plan->shape.max_batch);
+  if (chunk < 0 || (int64_t)batch * chunk * plan->shape.num_q_heads > (1 << 26))
+    return fail(KVQ_ERR_INVALID_ARG, "chunk %d: batch * chunk * Hq rows must be at most 2^26", chunk);
+  if (num_splits < 0 || num_splits > 1023) return fail(KVQ_ERR_INVALID_ARG, "num_splits %d", num_splits);
+  if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
+  if (max_seq_len > capacity_tokens(plan, nullptr))
+    return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > %lld tokens of capacity", max_seq_len,
+                (long long)capacity_tokens(plan, nullptr));
+  if (batch == 0 || chunk == 0) return ok();
+  const int32_t splits = num_splits ? num_splits : prefix_splits(plan, batch, chunk, max_seq_len);
+  const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
+  const int32_t gps = nvg > 0 ? (nvg + splits - 1) / splits : 1;
+  const size_t rows = (size_t)batch * chunk * plan->shape.num_q_heads;
+  const size_t need = rows * (splits + 1) * (kvq::D + 1) * sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if ((int64_t)splits * prefix_blocks(plan, chunk) > 0x7FFFFFFF)
+    return fail(KVQ_ERR_INVALID_ARG, "num_splits %d times the row blocks exceeds the grid", splits);
+  kvq::DecodeArgs a;
+  a.geo = geom(plan, layer, cache);
+  a.pg = paged_geom(plan, layer, nullptr);
+  a.q = q;
+  a.seq_lens = seq_lens;
+  a.splits = splits;
+  a.groups_per_split = gps;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.part_o = (float*)workspace;
+  a.part_lse = a.part_o + rows * (splits + 1) * kvq::D;
+  a.out = out;
+  a.out_f32 = 1;
+  a.lse_out = lse_out;
+  a.chunk = chunk;
+  a.part_stride = splits + 1;
+  a.k_chunk = k_chunk;
+  a.v_chunk = v_chunk;
+  hipStream_t s = (hipStream_t)stream;
+  kvq::EventPair ev;
+  bool timed = timer_slot(3, &ev);
+  hipError_t e = kvq::launch_prefix(a, batch, s, timed ? &ev : nullptr);
+  if (e != hipSuccess) return hip_status(e, "prefix split launch");
+  e = kvq::launch_chunk_causal(a, batch, s, nullptr);
+  if (e != hipSuccess) return hip_status(e, "chunk causal launch");
+  kvq::MergeArgs m;
+  m.part_o = a.part_o;
+  m.part_lse = a.part_lse;
+  m.splits = splits + 1;
+  m.rows = (int)rows;
+  m.out = out;
+  m.out_f32 = 1;
+  m.lse_out = lse_out;
+  timed = timer_slot(2, &ev);
+  e = kvq::launch_merge(m, s, timed ? &ev : nullptr);
+  return hip_status(e, "merge launch");
+}
+
 int kvq_dequantize(const kvq_plan* plan, int32_t layer, const void* cache, const int32_t* seq_lens, int32_t batch,
                    int32_t max_seq_len, float* k_out, float* v_out, const kvq_pages* pages, kvq_stream_t stream) {
   int st = check_plan_layer(plan, layer);

@@ -204,6 +204,13 @@ struct DecodeArgs {
   // Prefix attention: q holds `chunk` tokens a request, [batch][chunk][Hq][128],
   // and the rows of out (fp32), lse and the partials follow that order.
   int chunk = 0;
+  // Partials per row in the workspace (0 = splits). A chunked-prefill call
+  // keeps one more for the chunk's own causal part (partial index `splits`),
+  // so that the merge pass joins the prefix splits and the chunk part.
+  int part_stride = 0;
+  // Chunked prefill: the chunk's own fp16 keys and values, [batch][hkv][chunk][128].
+  const uint16_t* k_chunk = nullptr;
+  const uint16_t* v_chunk = nullptr;
 };
 
 struct MergeArgs {
@@ -227,6 +234,7 @@ hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s);
 hipError_t launch_decode_split_mfma(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_decode_paged(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_prefix(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
+hipError_t launch_chunk_causal(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev);
 int prefix_rows_per_block();  // query rows one prefix-attention workgroup takes
 hipError_t launch_append_paged(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev);
 hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s);

@@ -364,15 +364,173 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefix_kernel(DecodeArgs a) {
     const size_t orow = ((size_t)r * a.chunk + row / G) * g.hq + h * G + row % G;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const float lse = l > 0.f ? (acc.m[n] + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-    float* dst = a.splits == 1 ? (float*)a.out + orow * D : a.part_o + (orow * a.splits + split) * D;
+    const int ps = a.part_stride ? a.part_stride : a.splits;
+    float* dst = ps == 1 ? (float*)a.out + orow * D : a.part_o + (orow * ps + split) * D;
 #pragma unroll
     for (int u = 0; u < 8; ++u) *(f4_t*)(dst + 16 * u + 4 * a4) = acc.o[n][u] * inv;
     if (a4 == 0) {
-      if (a.splits > 1)
-        a.part_lse[orow * a.splits + split] = lse;
+      if (ps > 1)
+        a.part_lse[orow * ps + split] = lse;
       else if (a.lse_out)
         a.lse_out[orow] = lse;
     }
+  }
+}
+
+// ------------------------------------------------------ chunked prefill
+// The chunk's own part of chunked-prefill attention: each query row (chunk
+// token i, query head) over the chunk's fp16 keys and values 0 .. i, causally
+// (the chunk is not in the cache yet). Its (o, lse) is one more partial of the
+// row, which the merge pass joins with the prefix splits by log-sum-exp
+// (TriAxialKV page, "Facts": partial attentions merged by online
+// log-sum-exp). Keys and values are fp16 and q is fp16, so the score products
+// are exact with one fp16 operand each (no low planes); p is split into fp16
+// high and low parts as in the prefix pass.
+
+// Block kb of the chunk's keys and values (tokens 32 kb .. 32 kb + 31; those
+// at or past `chunk` become 0) into the record lane order of GroupBuf.
+__device__ __forceinline__ void load_chunk_block(const uint16_t* kc, const uint16_t* vc, int chunk, int kb, int w,
+                                                 int lane, GroupBuf& b) {
+  const int a = lane >> 4;
+  {  // key octet w: token 16(w/4) + lane%16, channels 32(w%4) + 8a .. + 7
+    const int t = 32 * kb + 16 * (w >> 2) + (lane & 15);
+    u4_t x = {0, 0, 0, 0};
+    if (t < chunk) x = *(const u4_t*)(kc + (size_t)t * D + 32 * (w & 3) + 8 * a);
+    b.khi[w][lane] = __builtin_bit_cast(h8_t, x);
+  }
+  {  // value octet w: channel 16w + lane%16, tokens 16(i/4) + 4a + i%4
+    h8_t x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 32 * kb + 16 * (i >> 2) + 4 * a + (i & 3);
+      const uint16_t bits = t < chunk ? vc[(size_t)t * D + 16 * w + (lane & 15)] : (uint16_t)0;
+      x[i] = __builtin_bit_cast(_Float16, bits);
+    }
+    b.vhi[w][lane] = x;
+  }
+}
+
+// One key block for the wave's column tiles; lim[n]: the last key (index in
+// the block) that column n's lane may see (its token minus 32 kb; < 0: none).
+__device__ __forceinline__ void chunk_step(const GroupBuf& b, const h8_t (*qv)[4], float scale_log2, int lane,
+                                           const int* lim, Acc& acc) {
+  const int a = lane >> 4;
+  f4_t c[kNT][2];
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) c[n][0] = c[n][1] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const h8_t k0 = b.khi[s][lane], k1 = b.khi[4 + s][lane];
+#pragma unroll
+    for (int n = 0; n < kNT; ++n) {
+      c[n][0] = mfma(k0, qv[n][s], c[n][0]);
+      c[n][1] = mfma(k1, qv[n][s], c[n][1]);
+    }
+  }
+  float hi[kNT];
+  bool raise = false;
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) {
+    hi[n] = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hi[n] = 16 * t + 4 * a + i <= lim[n] ? fmaxf(hi[n], c[n][t][i] * scale_log2) : hi[n];
+    raise = raise || hi[n] > acc.m[n] + kSlack;
+  }
+  if (__any(raise)) {
+#pragma unroll
+    for (int n = 0; n < kNT; ++n) {
+      const float mnew = fmaxf(acc.m[n], max_lane_groups(hi[n]));
+      const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(acc.m[n] - mnew);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc.o[n][u] *= alpha;
+      acc.lpart[n] *= alpha;
+      acc.m[n] = mnew;
+    }
+  }
+  h8_t ph[kNT], pl[kNT];
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) {
+    float p[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = 16 * t + 4 * a + i <= lim[n] && acc.m[n] != -INFINITY;
+        const float x = ok ? __builtin_amdgcn_exp2f(fmaf(c[n][t][i], scale_log2, -acc.m[n])) : 0.f;
+        p[4 * t + i] = x;
+        acc.lpart[n] += x;
+      }
+    split8(p, ph[n], pl[n]);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const h8_t vh = b.vhi[u][lane];
+#pragma unroll
+    for (int n = 0; n < kNT; ++n) {
+      acc.o[n][u] = mfma(vh, ph[n], acc.o[n][u]);
+      acc.o[n][u] = mfma(vh, pl[n], acc.o[n][u]);
+    }
+  }
+}
+
+// One workgroup per (block of kRows rows, KV head, request); writes partial
+// index a.splits of each row (a.part_stride partials a row).
+__global__ __launch_bounds__(kWaves * 64, 1) void chunk_causal_kernel(DecodeArgs a) {
+  __shared__ GroupBuf buf;
+  const LayerGeom& g = a.geo;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int blk = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
+  const int G = g.g, nrows = a.chunk * G;
+  const int row0 = blk * kRows + wave * (16 * kNT);
+  const size_t sigma = (size_t)r * g.hkv + h;
+  const uint16_t* kc = a.k_chunk + sigma * a.chunk * D;
+  const uint16_t* vc = a.v_chunk + sigma * a.chunk * D;
+  h8_t qv[kNT][4];
+  int tok[kNT];
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) {
+    const int row = min(row0 + 16 * n + (lane & 15), nrows - 1);
+    tok[n] = row / G;
+    const uint16_t* qp = a.q + (((size_t)r * a.chunk + row / G) * g.hq + h * G + row % G) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[n][s] = __builtin_bit_cast(h8_t, *(const u4_t*)(qp + 32 * s));
+  }
+  Acc acc;
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc.o[n][u] = f4_t{0.f, 0.f, 0.f, 0.f};
+    acc.m[n] = -INFINITY;
+    acc.lpart[n] = 0.f;
+  }
+  // key blocks up to the last token any row of the workgroup has
+  const int last = min((min(blk * kRows + kRows, nrows) - 1) / G, a.chunk - 1);
+  for (int kb = 0; kb <= last / GS; ++kb) {
+    load_chunk_block(kc, vc, a.chunk, kb, wave, lane, buf);
+    __syncthreads();
+    int lim[kNT];
+#pragma unroll
+    for (int n = 0; n < kNT; ++n) lim[n] = tok[n] - GS * kb;
+    chunk_step(buf, qv, a.scale_log2, lane, lim, acc);
+    __syncthreads();
+  }
+  const int a4 = lane >> 4;
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) {
+    const float l = sum_lane_groups(acc.lpart[n]);
+    const int row = row0 + 16 * n + (lane & 15);
+    if (row >= nrows) continue;
+    const size_t orow = ((size_t)r * a.chunk + row / G) * g.hq + h * G + row % G;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const float lse = l > 0.f ? (acc.m[n] + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+    float* dst = a.part_o + (orow * a.part_stride + a.splits) * D;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *(f4_t*)(dst + 16 * u + 4 * a4) = acc.o[n][u] * inv;
+    if (a4 == 0) a.part_lse[orow * a.part_stride + a.splits] = lse;
   }
 }
 
@@ -399,6 +557,12 @@ hipError_t launch_k(const DecodeArgs& a, int batch, hipStream_t s, const EventPa
 }  // namespace
 
 int prefix_rows_per_block() { return kRows; }
+
+hipError_t launch_chunk_causal(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
+  const int blocks = (a.chunk * a.geo.g + kRows - 1) / kRows;
+  if (blocks == 0 || batch == 0) return hipSuccess;
+  return launch_timed(chunk_causal_kernel, dim3(blocks, a.geo.hkv, batch), dim3(kWaves * 64), s, ev, a);
+}
 
 hipError_t launch_prefix(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
   switch (a.geo.kb) {
