@@ -310,15 +310,20 @@ size_t kvq_prefix_workspace_bytes(const kvq_plan *plan, int32_t batch, int32_t c
  *   workspace: device, kvq_prefix_workspace_bytes(...) bytes (may be NULL
  *     when that is 0); num_splits: 0 = automatic, else 1..1024;
  *   cache, q, out and workspace 16-byte aligned.
- * Query head h of a token uses KV head h / (Hq / Hkv). Contiguous plans only.
- *   Errors: INVALID_ARG (batch * chunk * Hq > 2^26 included), UNSUPPORTED (paged
- *   plan), CAPACITY (max_seq_len > max_tokens), WORKSPACE, HIP.
+ * Query head h of a token uses KV head h / (Hq / Hkv).
+ * Paged mode (pages != NULL, required for a paged plan; seq_lens ignored):
+ * the prefix is each request's INT2 tokens then its INT4 tokens
+ * (pages->int2_len, int4_len), as kvq_decode_attention reads them; any split
+ * count is allowed.
+ *   Errors: INVALID_ARG (batch * chunk * Hq > 2^26 included; pages given for a
+ *   contiguous plan or missing for a paged one), CAPACITY (max_seq_len past the
+ *   capacity), WORKSPACE, HIP.
  */
 int kvq_prefix_attention(const kvq_plan *plan, int32_t layer, const void *cache,
                          const uint16_t *q, int32_t chunk, const int32_t *seq_lens,
                          int32_t batch, int32_t max_seq_len, float softmax_scale, float *out,
                          float *lse_out, void *workspace, size_t workspace_bytes,
-                         int32_t num_splits, kvq_stream_t stream);
+                         int32_t num_splits, const kvq_pages *pages, kvq_stream_t stream);
 
 /* Workspace bytes kvq_chunk_prefill_attention needs: batch * chunk * Hq *
  * (splits + 1) * (128 + 1) fp32 (the prefix splits' partials and the chunk's
@@ -348,16 +353,17 @@ size_t kvq_chunk_prefill_workspace_bytes(const kvq_plan *plan, int32_t batch, in
  *   workspace: kvq_chunk_prefill_workspace_bytes(...) bytes (never 0 for a
  *     non-empty chunk); num_splits: 0 = automatic, else 1..1023 (prefix
  *     splits);
- *   cache, q, k_chunk, v_chunk, out and workspace 16-byte aligned.
- * Contiguous plans only.
- *   Errors: INVALID_ARG, UNSUPPORTED (paged plan), CAPACITY, WORKSPACE, HIP.
+ *   cache, q, k_chunk, v_chunk, out and workspace 16-byte aligned;
+ *   pages: as in kvq_prefix_attention (paged plans).
+ *   Errors: INVALID_ARG, CAPACITY, WORKSPACE, HIP.
  */
 int kvq_chunk_prefill_attention(const kvq_plan *plan, int32_t layer, const void *cache,
                                 const uint16_t *q, const uint16_t *k_chunk,
                                 const uint16_t *v_chunk, int32_t chunk, const int32_t *seq_lens,
                                 int32_t batch, int32_t max_seq_len, float softmax_scale,
                                 float *out, float *lse_out, void *workspace,
-                                size_t workspace_bytes, int32_t num_splits, kvq_stream_t stream);
+                                size_t workspace_bytes, int32_t num_splits,
+                                const kvq_pages *pages, kvq_stream_t stream);
 
 /*
  * kvq_dequantize -- the cache of one layer back in fp32, for checking:

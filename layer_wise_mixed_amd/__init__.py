@@ -109,12 +109,12 @@ def load():
     L.kvq_prefix_workspace_bytes.argtypes = [ctypes.POINTER(Plan), i32, i32, i32, i32]
     L.kvq_prefix_workspace_bytes.restype = ctypes.c_size_t
     L.kvq_prefix_attention.argtypes = [ctypes.POINTER(Plan), i32, P, P, i32, P, i32, i32, ctypes.c_float, P, P, P,
-                                       ctypes.c_size_t, i32, P]
+                                       ctypes.c_size_t, i32, ctypes.POINTER(Pages), P]
     L.kvq_prefix_attention.restype = ctypes.c_int
     L.kvq_chunk_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Plan), i32, i32, i32, i32]
     L.kvq_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
     L.kvq_chunk_prefill_attention.argtypes = [ctypes.POINTER(Plan), i32, P, P, P, P, i32, P, i32, i32, ctypes.c_float,
-                                              P, P, P, ctypes.c_size_t, i32, P]
+                                              P, P, P, ctypes.c_size_t, i32, ctypes.POINTER(Pages), P]
     L.kvq_chunk_prefill_attention.restype = ctypes.c_int
     L.kvq_dequantize.argtypes = [ctypes.POINTER(Plan), i32, P, P, i32, i32, P, P, ctypes.POINTER(Pages), P]
     L.kvq_dequantize.restype = ctypes.c_int
@@ -266,7 +266,7 @@ def prefix_workspace_bytes(plan: Plan, batch: int, chunk: int, max_seq_len: int,
 
 
 def prefix_attention(plan: Plan, layer: int, cache, q, seq_lens, max_seq_len: int, softmax_scale: float, out,
-                     lse=None, workspace=None, num_splits: int = 0, stream=None):
+                     lse=None, workspace=None, num_splits: int = 0, stream=None, pages: Pages | None = None):
     """Attention of a chunk of query tokens over each request's cached prefix (no mask).
     q: fp16 [batch, chunk, Hq, 128]; seq_lens: cached tokens per request; out: fp32 [batch, chunk, Hq, 128];
     lse: fp32 [batch, chunk, Hq] or None; workspace: prefix_workspace_bytes(...) bytes (None if 0)."""
@@ -276,11 +276,13 @@ def prefix_attention(plan: Plan, layer: int, cache, q, seq_lens, max_seq_len: in
     assert out.dtype == torch.float32 and out.is_contiguous() and out.shape == q.shape
     assert lse is None or (lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:3])
     batch, chunk = q.shape[0], q.shape[1]
-    _dev_i32(seq_lens, batch, "seq_lens")
+    if pages is None:
+        _dev_i32(seq_lens, batch, "seq_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kvq_prefix_attention(ctypes.byref(plan), layer, _ptr(cache), _ptr(q), chunk, _ptr(seq_lens), batch,
                                        max_seq_len, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
-                                       ws_bytes, num_splits, _stream(stream)))
+                                       ws_bytes, num_splits, None if pages is None else ctypes.byref(pages),
+                                       _stream(stream)))
 
 
 def chunk_prefill_workspace_bytes(plan: Plan, batch: int, chunk: int, max_seq_len: int, num_splits: int = 0) -> int:
@@ -288,7 +290,8 @@ def chunk_prefill_workspace_bytes(plan: Plan, batch: int, chunk: int, max_seq_le
 
 
 def chunk_prefill_attention(plan: Plan, layer: int, cache, q, k_chunk, v_chunk, seq_lens, max_seq_len: int,
-                            softmax_scale: float, out, lse=None, workspace=None, num_splits: int = 0, stream=None):
+                            softmax_scale: float, out, lse=None, workspace=None, num_splits: int = 0, stream=None,
+                            pages: Pages | None = None):
     """A prefill chunk's whole attention: the cached prefix as stored plus the chunk's own fp16 tokens,
     causally. q: fp16 [batch, chunk, Hq, 128]; k_chunk, v_chunk: fp16 [batch, Hkv, chunk, 128];
     out: fp32 [batch, chunk, Hq, 128]; lse: fp32 [batch, chunk, Hq] or None; workspace:
@@ -302,12 +305,14 @@ def chunk_prefill_attention(plan: Plan, layer: int, cache, q, k_chunk, v_chunk, 
     assert k_chunk.shape[0] == batch and k_chunk.shape[2] == chunk
     assert out.dtype == torch.float32 and out.is_contiguous() and out.shape == q.shape
     assert lse is None or (lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:3])
-    _dev_i32(seq_lens, batch, "seq_lens")
+    if pages is None:
+        _dev_i32(seq_lens, batch, "seq_lens")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kvq_chunk_prefill_attention(ctypes.byref(plan), layer, _ptr(cache), _ptr(q), _ptr(k_chunk),
                                               _ptr(v_chunk), chunk, _ptr(seq_lens), batch, max_seq_len,
                                               float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-                                              num_splits, _stream(stream)))
+                                              num_splits, None if pages is None else ctypes.byref(pages),
+                                              _stream(stream)))
 
 
 def dequantize(plan: Plan, layer: int, cache, seq_lens, batch: int, max_seq_len: int, k_out, v_out,

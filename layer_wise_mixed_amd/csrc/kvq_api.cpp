@@ -487,11 +487,11 @@ size_t kvq_prefix_workspace_bytes(const kvq_plan* plan, int32_t batch, int32_t c
 int kvq_prefix_attention(const kvq_plan* plan, int32_t layer, const void* cache, const uint16_t* q, int32_t chunk,
                          const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float softmax_scale,
                          float* out, float* lse_out, void* workspace, size_t workspace_bytes, int32_t num_splits,
-                         kvq_stream_t stream) {
+                         const kvq_pages* pages, kvq_stream_t stream) {
   int st = check_plan_layer(plan, layer);
   if (st) return st;
-  if (is_paged(plan)) return fail(KVQ_ERR_UNSUPPORTED, "prefix attention reads contiguous streams only");
-  if (!cache || !q || !out || !seq_lens) return fail(KVQ_ERR_INVALID_ARG, "null cache, q, seq_lens or out");
+  if ((st = check_pages(plan, pages))) return st;
+  if (!cache || !q || !out || (!pages && !seq_lens)) return fail(KVQ_ERR_INVALID_ARG, "null cache, q, seq_lens or out");
   if (!aligned16(cache) || !aligned16(q) || !aligned16(out) || !aligned16(workspace))
     return fail(KVQ_ERR_INVALID_ARG, "cache, q, out and workspace must be 16-byte aligned");
   if (batch < 0 || batch > plan->shape.max_batch)
@@ -501,13 +501,13 @@ int kvq_prefix_attention(const kvq_plan* plan, int32_t layer, const void* cache,
   if (num_splits < 0 || num_splits > 1024) return fail(KVQ_ERR_INVALID_ARG, "num_splits %d", num_splits);
   if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
-  if (max_seq_len > capacity_tokens(plan, nullptr))
+  if (max_seq_len > capacity_tokens(plan, pages))
     return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > %lld tokens of capacity", max_seq_len,
-                (long long)capacity_tokens(plan, nullptr));
+                (long long)capacity_tokens(plan, pages));
   if (batch == 0 || chunk == 0) return ok();
   const int32_t splits = num_splits ? num_splits : prefix_splits(plan, batch, chunk, max_seq_len);
   const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
-  const int32_t gps = (nvg + splits - 1) / splits;
+  const int32_t gps = nvg > 0 ? (nvg + splits - 1) / splits : 1;
   const size_t rows = (size_t)batch * chunk * plan->shape.num_q_heads;
   const size_t need = splits > 1 ? rows * splits * (kvq::D + 1) * sizeof(float) : 0;
   if (need && (!workspace || workspace_bytes < need))
@@ -516,7 +516,7 @@ int kvq_prefix_attention(const kvq_plan* plan, int32_t layer, const void* cache,
     return fail(KVQ_ERR_INVALID_ARG, "num_splits %d times the row blocks exceeds the grid", splits);
   kvq::DecodeArgs a;
   a.geo = geom(plan, layer, cache);
-  a.pg = paged_geom(plan, layer, nullptr);
+  a.pg = paged_geom(plan, layer, pages);
   a.q = q;
   a.seq_lens = seq_lens;
   a.splits = splits;
@@ -558,11 +558,11 @@ int kvq_chunk_prefill_attention(const kvq_plan* plan, int32_t layer, const void*
                                 const uint16_t* k_chunk, const uint16_t* v_chunk, int32_t chunk,
                                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float softmax_scale,
                                 float* out, float* lse_out, void* workspace, size_t workspace_bytes,
-                                int32_t num_splits, kvq_stream_t stream) {
+                                int32_t num_splits, const kvq_pages* pages, kvq_stream_t stream) {
   int st = check_plan_layer(plan, layer);
   if (st) return st;
-  if (is_paged(plan)) return fail(KVQ_ERR_UNSUPPORTED, "chunked prefill reads contiguous streams only");
-  if (!cache || !q || !k_chunk || !v_chunk || !out || !seq_lens)
+  if ((st = check_pages(plan, pages))) return st;
+  if (!cache || !q || !k_chunk || !v_chunk || !out || (!pages && !seq_lens))
     return fail(KVQ_ERR_INVALID_ARG, "null cache, q, k_chunk, v_chunk, seq_lens or out");
   if (!aligned16(cache) || !aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(out) ||
       !aligned16(workspace))
@@ -574,9 +574,9 @@ int kvq_chunk_prefill_attention(const kvq_plan* plan, int32_t layer, const void*
   if (num_splits < 0 || num_splits > 1023) return fail(KVQ_ERR_INVALID_ARG, "num_splits %d", num_splits);
   if (!std::isfinite(softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (max_seq_len < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len %d < 0", max_seq_len);
-  if (max_seq_len > capacity_tokens(plan, nullptr))
+  if (max_seq_len > capacity_tokens(plan, pages))
     return fail(KVQ_ERR_CAPACITY, "max_seq_len %d > %lld tokens of capacity", max_seq_len,
-                (long long)capacity_tokens(plan, nullptr));
+                (long long)capacity_tokens(plan, pages));
   if (batch == 0 || chunk == 0) return ok();
   const int32_t splits = num_splits ? num_splits : prefix_splits(plan, batch, chunk, max_seq_len);
   const int32_t nvg = (max_seq_len + kvq::GS - 1) / kvq::GS;
@@ -602,6 +602,7 @@ int kvq_chunk_prefill_attention(const kvq_plan* plan, int32_t layer, const void*
   a.lse_out = lse_out;
   a.chunk = chunk;
   a.part_stride = splits + 1;
+  a.pg = paged_geom(plan, layer, pages);
   a.k_chunk = k_chunk;
   a.v_chunk = v_chunk;
   hipStream_t s = (hipStream_t)stream;

@@ -286,6 +286,34 @@ __device__ __forceinline__ void group_step(const GroupBuf& b, const h8_t (*qv)[4
   }
 }
 
+// The wave's rows: o = O / l, lse = (m + log2 l) ln 2, into the output (one
+// partial a row) or into partial `split` of a.part_stride (or a.splits) a row.
+__device__ __forceinline__ void store_rows(const DecodeArgs& a, const Acc& acc, int row0, int nrows, int r, int h,
+                                           int split, int lane) {
+  const LayerGeom& g = a.geo;
+  const int G = g.g;
+  const int a4 = lane >> 4;
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) {
+    const float l = sum_lane_groups(acc.lpart[n]);
+    const int row = row0 + 16 * n + (lane & 15);
+    if (row >= nrows) continue;
+    const size_t orow = ((size_t)r * a.chunk + row / G) * g.hq + h * G + row % G;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const float lse = l > 0.f ? (acc.m[n] + __log2f(l)) * 0.69314718055994531f : -INFINITY;
+    const int ps = a.part_stride ? a.part_stride : a.splits;
+    float* dst = ps == 1 ? (float*)a.out + orow * D : a.part_o + (orow * ps + split) * D;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *(f4_t*)(dst + 16 * u + 4 * a4) = acc.o[n][u] * inv;
+    if (a4 == 0) {
+      if (ps > 1)
+        a.part_lse[orow * ps + split] = lse;
+      else if (a.lse_out)
+        a.lse_out[orow] = lse;
+    }
+  }
+}
+
 // One workgroup per (split, block of kRows rows, KV head, request), split
 // fastest. Rows of a (request, KV head): row i is chunk token i / G, query
 // head h G + i % G; q and the outputs are [request][token][Hq] rows.
@@ -354,27 +382,111 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefix_kernel(DecodeArgs a) {
     group_step<true>(buf[nk & 1], qv, a.scale_log2, lane, T, acc);
   }
 
-  // the wave's rows: o = O / l, lse = (m + log2 l) ln 2
-  const int a4 = lane >> 4;
+  store_rows(a, acc, row0, nrows, r, h, split, lane);
+}
+
+// Paged pool: a request's INT2 tokens (K2V2 records in page pairs) and then
+// its INT4 tokens (page pairs of per-token 4-bit keys and values, the last
+// pair partly filled), as one sequence of 32-token groups that the splits
+// share out (TriAxialKV page, "Facts": page pools and page tables).
+
+// One INT4 page pair (tokens 0..31 of it: page a holds 0..15, page b
+// 16..31) into LDS: the thread's key and value octets dequantized straight
+// from the pages (fmaf(code, scale, zero), per-token meta); tokens at or past
+// ntok become 0.
+__device__ __forceinline__ void dequant_int4_pair(const uint8_t* pa, const uint8_t* pb, int ntok, GroupBuf& b, int w,
+                                                  int lane) {
+  const int a = lane >> 4;
+  float x[8];
+  {  // key octet w: token 16(w/4) + lane%16, channels 32(w%4) + 8a + i
+    const int t = 16 * (w >> 2) + (lane & 15);
+    const uint8_t* pg = t < PAGE_TOKENS ? pa : pb;
+    const int p = t & 15;
+    const float* km = (const float*)(pg + INT4_KMETA);
+    const int mi = 16 * (w & 3) + p;
+    const float sc = km[mi], zr = km[64 + mi];
 #pragma unroll
-  for (int n = 0; n < kNT; ++n) {
-    const float l = sum_lane_groups(acc.lpart[n]);
-    const int row = row0 + 16 * n + (lane & 15);
-    if (row >= nrows) continue;
-    const size_t orow = ((size_t)r * a.chunk + row / G) * g.hq + h * G + row % G;
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const float lse = l > 0.f ? (acc.m[n] + __log2f(l)) * 0.69314718055994531f : -INFINITY;
-    const int ps = a.part_stride ? a.part_stride : a.splits;
-    float* dst = ps == 1 ? (float*)a.out + orow * D : a.part_o + (orow * ps + split) * D;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) *(f4_t*)(dst + 16 * u + 4 * a4) = acc.o[n][u] * inv;
-    if (a4 == 0) {
-      if (ps > 1)
-        a.part_lse[orow * ps + split] = lse;
-      else if (a.lse_out)
-        a.lse_out[orow] = lse;
+    for (int i = 0; i < 8; ++i) {
+      int sh;
+      const uint32_t off = page_k_offset(p, 32 * (w & 3) + 8 * a + i, &sh);
+      const float code = (float)((*(const uint32_t*)(pg + off) >> sh) & 15u);
+      x[i] = t < ntok ? fmaf(code, sc, zr) : 0.f;
     }
   }
+  split8(x, b.khi[w][lane], b.klo[w][lane]);
+  {  // value octet w: channel 16w + lane%16, tokens 16(i/4) + 4a + i%4
+    const int c = 16 * w + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 16 * (i >> 2) + 4 * a + (i & 3);
+      const uint8_t* pg = j < PAGE_TOKENS ? pa : pb;
+      const int p = j & 15;
+      int sh;
+      const uint32_t off = page_v_offset(p, c, &sh);
+      const float code = (float)((*(const uint32_t*)(pg + off) >> sh) & 15u);
+      const float* vm = (const float*)(pg + INT4_VMETA);
+      const int mi = 16 * (c >> 5) + p;
+      x[i] = j < ntok ? fmaf(code, vm[mi], vm[64 + mi]) : 0.f;
+    }
+  }
+  split8(x, b.vhi[w][lane], b.vlo[w][lane]);
+}
+
+__global__ __launch_bounds__(kWaves * 64, 1) void prefix_paged_kernel(DecodeArgs a) {
+  __shared__ GroupBuf buf;
+  const LayerGeom& g = a.geo;
+  const PagedGeom& pg = a.pg;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x % a.splits, blk = blockIdx.x / a.splits;
+  const int h = blockIdx.y, r = blockIdx.z;
+  const int n2 = max(pg.int2_len[r], 0), n4 = max(pg.int4_len[r], 0);
+  const int n2g = n2 / GS, nvg = n2g + (n4 + GS - 1) / GS;
+  const int g0 = split * a.groups_per_split;
+  const int g1 = min(g0 + a.groups_per_split, nvg);
+  const int32_t* table = pg.table + (size_t)r * pg.max_pages;
+  const int G = g.g, nrows = a.chunk * G;
+  const int row0 = blk * kRows + wave * (16 * kNT);
+  h8_t qv[kNT][4];
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) {
+    const int row = min(row0 + 16 * n + (lane & 15), nrows - 1);
+    const uint16_t* qp = a.q + (((size_t)r * a.chunk + row / G) * g.hq + h * G + row % G) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[n][s] = __builtin_bit_cast(h8_t, *(const u4_t*)(qp + 32 * s));
+  }
+  Acc acc;
+#pragma unroll
+  for (int n = 0; n < kNT; ++n) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc.o[n][u] = f4_t{0.f, 0.f, 0.f, 0.f};
+    acc.m[n] = -INFINITY;
+    acc.lpart[n] = 0.f;
+  }
+  for (int gi = g0; gi < g1; ++gi) {  // workgroup-uniform branches
+    int ntok = GS;
+    if (gi < n2g) {
+      const uint8_t* rec = g.base + (size_t)table[2 * gi] * pg.int2_page_bytes + (size_t)h * INT2_RECORD;
+      Share<2, 2, false> sh;
+      load_share<2, 2, false>(rec, wave, lane, sh);
+      dequant_share<2, 2, false, false>(sh, buf, wave, lane, GS);
+    } else {
+      const int i = gi - n2g;
+      const int e = n2 / PAGE_TOKENS + 2 * i;
+      ntok = min(GS, n4 - GS * i);
+      const uint8_t* base4 = g.base + pg.int4_offset + (size_t)h * INT4_HEAD;
+      const uint8_t* pa = base4 + (size_t)(table[e] - pg.int2_pages) * pg.int4_page_bytes;
+      const uint8_t* pb = ntok > PAGE_TOKENS ? base4 + (size_t)(table[e + 1] - pg.int2_pages) * pg.int4_page_bytes : pa;
+      dequant_int4_pair(pa, pb, ntok, buf, wave, lane);
+    }
+    __syncthreads();
+    if (ntok == GS)
+      group_step<false>(buf, qv, a.scale_log2, lane, GS, acc);
+    else
+      group_step<true>(buf, qv, a.scale_log2, lane, ntok, acc);
+    __syncthreads();
+  }
+  store_rows(a, acc, row0, nrows, r, h, split, lane);
 }
 
 // ------------------------------------------------------ chunked prefill
@@ -565,6 +677,10 @@ hipError_t launch_chunk_causal(const DecodeArgs& a, int batch, hipStream_t s, co
 }
 
 hipError_t launch_prefix(const DecodeArgs& a, int batch, hipStream_t s, const EventPair* ev) {
+  if (a.pg.table) {
+    const int blocks = (a.chunk * a.geo.g + kRows - 1) / kRows;
+    return launch_timed(prefix_paged_kernel, dim3(a.splits * blocks, a.geo.hkv, batch), dim3(kWaves * 64), s, ev, a);
+  }
   switch (a.geo.kb) {
     case 2: return launch_k<2>(a, batch, s, ev);
     case 4: return launch_k<4>(a, batch, s, ev);

@@ -71,13 +71,3 @@ def test_chunk_prefill_matches_oracle(gpu, oq, G, chunk, splits):
         assert np.isfinite(out).all()
 
 
-def test_chunk_prefill_refuses_paged_plans(gpu):
-    plan = gpu.plan_layers(gpu.make_shape(8, 2, 2, page_tokens=16, int2_pages=4, int4_pages=4), [(2, 2, 0, 1)])
-    lib = gpu.load()
-    import ctypes
-
-    st = lib.kvq_chunk_prefill_attention(ctypes.byref(plan), 0, ctypes.c_void_p(256), ctypes.c_void_p(256),
-                                         ctypes.c_void_p(256), ctypes.c_void_p(256), 4, ctypes.c_void_p(256), 2, 16,
-                                         ctypes.c_float(SCALE), ctypes.c_void_p(256), None, ctypes.c_void_p(256),
-                                         1 << 20, 0, None)
-    assert st == gpu.ERR_UNSUPPORTED

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import synthetic as syn
-from test_gpu_parity import LSE_ABS, MAX_ABS, REL_L2
+from test_gpu_parity import LSE_ABS, MAX_ABS, REL_L2, check_attention
 
 pytestmark = pytest.mark.gpu
 PAGE = 16
@@ -302,3 +302,59 @@ def test_fused_paged_step_at_pair_boundaries(bounds, splits):
     """The fused paged step where the new token completes a page pair, opens one, or lands in
     a pair its wave reads second: bit for bit the separate calls' pool, output and lse."""
     _fused_vs_separate(bounds, 4, splits)
+
+
+@pytest.mark.parametrize("case,chunk,splits", [("small", 5, 0), ("small", 40, 3), ("long", 9, 0), ("long", 33, 2)])
+def test_paged_prefix_and_chunk_prefill(case, chunk, splits, request, oq):
+    """Chunked prefill over a paged pool: kvq_prefix_attention (every chunk row over the request's
+    INT2 then INT4 tokens, no mask) and kvq_chunk_prefill_attention (plus the chunk's own fp16
+    tokens, causally) against fp64 attention over the oracle's own unpacking of the same pool."""
+    c = request.getfixturevalue(case)
+    kvq = c.kvq
+    G = c.hq // c.hkv
+    ml = c.max_len()
+    q = syn.queries_steps_fp16(c.seed, 0, c.batch, c.hq, 900, chunk).permute(0, 2, 1, 3).contiguous()
+    kc = syn.keys_fp16(c.seed + 7, 0, range(c.batch), range(c.hkv), 0, chunk, num_kv_heads=c.hkv).contiguous()
+    vc = syn.values_fp16(c.seed + 7, 0, range(c.batch), range(c.hkv), 0, chunk).contiguous()
+    pool = c.oracle_pool(0)
+    tb = c.table.cpu().numpy()
+    scale = 1 / math.sqrt(128)
+    ref_p = np.zeros((c.batch, chunk, c.hq, 128))
+    lse_p = np.zeros((c.batch, chunk, c.hq))
+    ref_c = np.zeros_like(ref_p)
+    lse_c = np.zeros_like(lse_p)
+    for r in range(c.batch):
+        for h in range(c.hkv):
+            kd, vd = oq.unpack_paged(pool, c.n2[r], c.n4[r], tb[r], c.int2_pages, c.hkv, h)
+            rows = q[r, :, h * G:(h + 1) * G].reshape(chunk * G, 128).numpy()
+            o, ls = oq.attention(rows, kd, vd, scale)
+            ref_p[r, :, h * G:(h + 1) * G] = o.reshape(chunk, G, 128)
+            lse_p[r, :, h * G:(h + 1) * G] = ls.reshape(chunk, G)
+            kcf = kc[r, h].numpy().astype(np.float32)
+            vcf = vc[r, h].numpy().astype(np.float32)
+            for i in range(chunk):
+                o, ls = oq.attention(q[r, i, h * G:(h + 1) * G].numpy(), np.concatenate([kd, kcf[:i + 1]]),
+                                     np.concatenate([vd, vcf[:i + 1]]), scale)
+                ref_c[r, i, h * G:(h + 1) * G] = o
+                lse_c[r, i, h * G:(h + 1) * G] = ls
+    n = c.batch * chunk
+    lens = [c.n2[r] + c.n4[r] for r in range(c.batch) for _ in range(chunk)]
+    # prefix part alone
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    wsb = kvq.prefix_workspace_bytes(c.plan, c.batch, chunk, ml, splits)
+    ws = torch.empty(wsb // 4 + 1, dtype=torch.float32, device="cuda") if wsb else None
+    kvq.prefix_attention(c.plan, 0, c.pool, q.cuda(), None, ml, scale, out, lse, ws, splits, pages=c.pages())
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy().reshape(n, c.hq, 128), lse.cpu().numpy().reshape(n, c.hq),
+                    ref_p.reshape(n, c.hq, 128), lse_p.reshape(n, c.hq), lens, c.hq, c.hkv)
+    # the whole chunked-prefill attention
+    out.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    wsb = kvq.chunk_prefill_workspace_bytes(c.plan, c.batch, chunk, ml, splits)
+    ws = torch.empty(wsb // 4 + 1, dtype=torch.float32, device="cuda")
+    kvq.chunk_prefill_attention(c.plan, 0, c.pool, q.cuda(), kc.cuda(), vc.cuda(), None, ml, scale, out, lse, ws,
+                                splits, pages=c.pages())
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy().reshape(n, c.hq, 128), lse.cpu().numpy().reshape(n, c.hq),
+                    ref_c.reshape(n, c.hq, 128), lse_c.reshape(n, c.hq), [1] * n, c.hq, c.hkv)

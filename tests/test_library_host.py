@@ -262,7 +262,7 @@ def test_prefix_attention_argument_errors(lib):
              ws=True):
         return lib.kvq_prefix_attention(ctypes.byref(plan), layer, f, q, chunk, f if seq else None, batch,
                                         max_seq_len, ctypes.c_float(0.088), f, None, f if ws else None, ws_bytes,
-                                        splits, None)
+                                        splits, None, None)
 
     assert call(layer=2) == kvq.ERR_INVALID_ARG
     assert call(batch=5) == kvq.ERR_INVALID_ARG
@@ -276,7 +276,7 @@ def test_prefix_attention_argument_errors(lib):
     assert call(seq=False) == kvq.ERR_INVALID_ARG
     assert call(q=odd) == kvq.ERR_INVALID_ARG
     assert "16-byte" in lib.kvq_last_error().decode()
-    assert call(plan=_paged_plan()) == kvq.ERR_UNSUPPORTED
+    assert call(plan=_paged_plan()) == kvq.ERR_INVALID_ARG  # a paged plan needs its pages
     assert call(batch=0) == kvq.OK and call(chunk=0) == kvq.OK  # nothing to do
 
 
