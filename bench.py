@@ -24,6 +24,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -70,10 +72,12 @@ WORKLOADS = {
 # per-token), the rest and every decoded token INT4 per-token; tables in seeded page order.
 PAGED_WORKLOADS = {
     "paged-b16-l32768-int2int4": dict(layers=36, hq=32, hkv=8, batch=16, prefill=32767, cycle=32,
-                                      outliers=(4, 10.0),
+                                      outliers=(4, 10.0), tags=8, budget=3.0,
                                       desc="36 layers, 32/8 heads, batch 16, context 32768..32799 in a paged pool: "
-                                           "16384 INT2 tokens (seeded 32-token runs) + 16384..16415 INT4 tokens, "
-                                           "3.0 bits at context 32768"),
+                                           "8 seeded role tags a request, each INT2 or INT4 by the allocator from "
+                                           "D_k(b) measured with the library on a calibration sample at a 3.0-bit "
+                                           "budget; the INT2 tags' tokens in 32-token groups, the rest and every "
+                                           "decoded token INT4"),
 }
 WORKLOADS.update({k: dict(v, paged=True) for k, v in PAGED_WORKLOADS.items()})
 DEFAULT_WORKLOAD = "llama31-8b-b64-mixed325-l2048"
@@ -269,16 +273,27 @@ class PagedWorkload:
         self.P, self.C = w["prefill"], w["cycle"]
         self.outliers = w["outliers"]
         self.scale = 1.0 / math.sqrt(128.0)
-        runs = self.P // 32
-        # INT2 tokens per request: 512 of the prompt's 1023 full 32-token runs, 16384 tokens, so that
-        # at the first decode step half of the cache (16384 of 32768 tokens) is INT2: 3.0 bits
-        self.n2 = 32 * ((runs + 1) // 2)
-        n4_cap = self.P - self.n2 + self.C
-        pairs_per_req = self.n2 // 32
-        quads_per_req = -(-n4_cap // self.PAGE)
-        self.int2_pages = 2 * pairs_per_req * self.B
-        self.int4_pages = quads_per_req * self.B
-        self.max_pages = 2 * pairs_per_req + quads_per_req
+        # which prompt tokens are INT2: each request's tokens carry seeded role tags; D_k(b) of every
+        # tag, measured with the library's kernels on a calibration sample (two requests, 2048
+        # tokens, this workload's head shape), feeds the allocator at the workload's bit budget; the
+        # INT2 tags' tokens form 32-token groups in arrival order, the rest go INT4
+        from layer_wise_mixed_amd.allocate import int2_tokens
+        from layer_wise_mixed_amd.distortion import calibrate
+
+        self.num_tags, self.budget = w["tags"], w["budget"]
+        self.D, self.tag_bits, _ = calibrate(self.Hq, self.Hkv, self.num_tags, self.budget, batch=2, seq_len=2048,
+                                             seed=seed, outliers=self.outliers, device=device)
+        self.orders, self.n2s = [], []
+        for r in range(self.B):
+            tags = syn.seeded_tags(seed, r, self.P, self.num_tags)
+            a2, a4 = int2_tokens(tags, self.tag_bits)
+            self.orders.append(a2 + a4)
+            self.n2s.append(len(a2))
+        pairs_r = [n2 // 32 for n2 in self.n2s]
+        quads_r = [-(-(self.P - n2 + self.C) // self.PAGE) for n2 in self.n2s]
+        self.int2_pages = 2 * sum(pairs_r)
+        self.int4_pages = sum(quads_r)
+        self.max_pages = max(2 * p + q for p, q in zip(pairs_r, quads_r))
         shape = kvq.make_shape(self.Hq, self.Hkv, self.B, page_tokens=self.PAGE, int2_pages=self.int2_pages,
                                int4_pages=self.int4_pages)
         self.plan = kvq.plan_layers(shape, [(2, 2, 0, 1)] * self.L)
@@ -286,15 +301,18 @@ class PagedWorkload:
         # seeded physical page order, one table per request (shared by all layers)
         pairs = syn.seeded_permutation(seed, syn.T_PAGE, self.int2_pages // 2)
         quads = syn.seeded_permutation(seed, syn.T_PAGE, self.int4_pages, salt=1)
-        table = []
+        table = np.zeros((self.B, self.max_pages), np.int32)
+        p0, q0 = 0, 0
         for r in range(self.B):
-            row = [x for p in pairs[r * pairs_per_req:(r + 1) * pairs_per_req] for x in (2 * p, 2 * p + 1)]
-            row += [self.int2_pages + q for q in quads[r * quads_per_req:(r + 1) * quads_per_req]]
-            table.append(row)
-        self.table = torch.tensor(table, dtype=torch.int32, device=device)
+            row = [x for p in pairs[p0:p0 + pairs_r[r]] for x in (2 * p, 2 * p + 1)]
+            row += [self.int2_pages + q for q in quads[q0:q0 + quads_r[r]]]
+            p0 += pairs_r[r]
+            q0 += quads_r[r]
+            table[r, :len(row)] = row
+        self.table = torch.from_numpy(table).to(device)
         self.num_splits = num_splits
         zero = torch.zeros(self.B, dtype=torch.int32, device=device)
-        add2 = torch.full((self.B,), self.n2, dtype=torch.int32, device=device)
+        add2 = torch.tensor(self.n2s, dtype=torch.int32, device=device)
         orders = [torch.tensor(self._prompt_order(r), dtype=torch.int64, device=device) for r in range(self.B)]
         for l, li in enumerate(self.layer_ids):  # prefill one request at a time: INT2 runs first, then the rest
             for r in range(self.B):
@@ -313,8 +331,8 @@ class PagedWorkload:
             self.v_dec.append(v.permute(2, 0, 1, 3).contiguous().unsqueeze(3))
             qq = syn.queries_steps_fp16(seed, li, self.B, self.Hq, 0, self.C, device=device)
             self.q.append(qq.permute(2, 0, 1, 3).contiguous())
-        self.n2_dev = torch.full((self.B,), self.n2, dtype=torch.int32, device=device)
-        self.n4_base = torch.full((self.B,), self.P - self.n2, dtype=torch.int32, device=device)
+        self.n2_dev = torch.tensor(self.n2s, dtype=torch.int32, device=device)
+        self.n4_base = torch.tensor([self.P - n2 for n2 in self.n2s], dtype=torch.int32, device=device)
         self.n4_before = self.n4_base.clone()
         self.n4_after = self.n4_base + 1
         self.pages_append = kvq.make_pages(self.table, self.max_pages, self.n2_dev, self.n4_before)
@@ -328,13 +346,15 @@ class PagedWorkload:
         torch.cuda.synchronize()
 
     def _prompt_order(self, r):
-        """Token indices of request r's prompt in append order: its INT2 runs (seeded choice of
-        half of the 32-token runs, in arrival order), then every other token in arrival order."""
-        runs = self.P // 32
-        chosen = set(syn.seeded_choice(self.seed, syn.T_TAG, runs, self.n2 // 32, salt=r))
-        first = [t for j in sorted(chosen) for t in range(32 * j, 32 * j + 32)]
-        rest = [t for t in range(self.P) if t // 32 not in chosen or t >= 32 * runs]
-        return first + rest
+        """Token indices of request r's prompt in append order: the tokens of its INT2 tags that fill
+        whole 32-token groups, in arrival order, then every other token in arrival order."""
+        return list(self.orders[r])
+
+    def equiv_bits(self):
+        """Mean code bits per cached token at the first decode step (INT2 2, INT4 4)."""
+        n2 = sum(self.n2s)
+        total = self.B * (self.P + 1)
+        return (2.0 * n2 + 4.0 * (total - n2)) / total
 
     def keys(self, layer, requests, t0, n, device):
         cnt, fac = self.outliers
@@ -366,8 +386,10 @@ class PagedWorkload:
     def split_bytes(self, i):
         """Algorithmic bytes the split passes of step i read: INT2 group records (codes + meta),
         INT4 tokens (codes + meta, 192 B per token and KV head), and q."""
-        n4 = self.P - self.n2 + i + 1
-        per_layer = self.B * self.Hkv * ((self.n2 // 32) * 4096 + n4 * 192) + self.B * self.Hq * 256
+        per_layer = self.B * self.Hq * 256
+        for n2 in self.n2s:
+            n4 = self.P - n2 + i + 1
+            per_layer += self.Hkv * ((n2 // 32) * 4096 + n4 * 192)
         return per_layer * self.L
 
 
@@ -423,7 +445,6 @@ def cpu_baseline_paged(wl, positions, max_seconds=15.0):
     (request, KV head) streams of layer 0 into its own pool through the same page tables, each
     stream at the INT4 length of one of the timed cycle positions, then times unpack +
     dequantize + fp64 attention on all host threads (up to 16) and on one thread."""
-    import numpy as np
 
     import oracle
 
@@ -437,19 +458,21 @@ def cpu_baseline_paged(wl, positions, max_seconds=15.0):
     for s in range(n_streams):
         r, h = divmod(s, wl.Hkv)
         pos = positions[s % len(positions)]
-        n4 = wl.P - wl.n2 + pos + 1
+        n4 = wl.P - wl.n2s[r] + pos + 1
         order = wl._prompt_order(r) + list(range(wl.P, wl.P + pos + 1))
         k = syn.keys_fp16(wl.seed, layer, [r], [h], 0, wl.P + pos + 1, outlier_count=cnt, outlier_factor=fac,
                           num_kv_heads=wl.Hkv)[0, 0].numpy()[order]
         v = syn.values_fp16(wl.seed, layer, [r], [h], 0, wl.P + pos + 1)[0, 0].numpy()[order]
-        oracle.pack_paged(pool, k, v, wl.n2, tables[r], wl.int2_pages, wl.Hkv, h)
+        oracle.pack_paged(pool, k, v, wl.n2s[r], tables[r], wl.int2_pages, wl.Hkv, h)
         req.append(r)
         head.append(h)
         n4s.append(n4)
         qs[s] = syn.queries_fp16(wl.seed, layer, pos, r + 1, wl.Hq)[r, h * G:(h + 1) * G].numpy()
 
+    n2s = [wl.n2s[r] for r in req]
+
     def run(ns, threads):
-        return oracle.decode_paged(pool, req[:ns], head[:ns], [wl.n2] * ns, n4s[:ns], tables, wl.int2_pages,
+        return oracle.decode_paged(pool, req[:ns], head[:ns], n2s[:ns], n4s[:ns], tables, wl.int2_pages,
                                    wl.Hkv, qs[:ns], G, wl.scale, threads)[2]
 
     dt, reps, used = _timed_reps(lambda: run(n_streams, _threads()), max_seconds)
@@ -460,7 +483,8 @@ def cpu_baseline_paged(wl, positions, max_seconds=15.0):
     return {"value": wl.B / t_step, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "value_1thread": wl.B / t_step1,
             "sample": f"{n_streams} (request, KV head) streams of layer 0, each at the length of one of the timed "
-                      f"cycle positions ({wl.n2} INT2 + {min(n4s)}..{max(n4s)} INT4 tokens), repeated {reps}x "
+                      f"cycle positions ({min(n2s)}..{max(n2s)} INT2 + {min(n4s)}..{max(n4s)} INT4 tokens), "
+                      f"repeated {reps}x "
                       f"({dt * 1e3:.1f} ms each) on {int(used)} threads, and {n1} streams {reps1}x on 1 thread; "
                       f"step time scaled to {wl.B * wl.Hkv} streams x {wl.L} layers"}
 
@@ -470,7 +494,6 @@ def cpu_baseline(wl, positions, max_seconds=15.0):
     KV head) streams of layer 0, each at the cache length of one of the timed cycle positions,
     packed by the oracle into its own layer; it unpacks + dequantizes them and runs fp64
     attention, on all host threads (up to 16) and on one thread."""
-    import numpy as np
 
     import oracle
 
@@ -610,10 +633,12 @@ def roofline_obj(m, fused):
 def workload_config(wl, m, fused, graph):
     return {"workload": wl.name, "description": wl.w["desc"], "layers": wl.L, "batch": wl.B,
             "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": 128, "context": m["context"],
-            "equiv_bits": wl.plan.equiv_bits, "splits": wl.splits,
+            "equiv_bits": wl.equiv_bits() if hasattr(wl, "equiv_bits") else wl.plan.equiv_bits, "splits": wl.splits,
             "launch": ("hip-graph per step" if graph else "eager")
             + ("; token append fused into the split pass" if fused else "; append kernel, then split pass"),
-            "effective_GBps_whole_step": m["eff_gbs"], "effective_frac_whole_step": m["eff_gbs"] / HBM_PEAK_GBS}
+            "effective_GBps_whole_step": m["eff_gbs"], "effective_frac_whole_step": m["eff_gbs"] / HBM_PEAK_GBS,
+            **({"tag_bits": list(map(int, wl.tag_bits)), "int2_tokens_per_request": [min(wl.n2s), max(wl.n2s)]}
+               if hasattr(wl, "tag_bits") else {})}
 
 
 def make_workload(name, args):

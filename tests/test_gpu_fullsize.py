@@ -129,12 +129,12 @@ def test_fullsize_paged(gpu, oq, positions):
         if pos not in positions:
             continue
         torch.cuda.synchronize()
-        n2, n4 = wl.n2, wl.P - wl.n2 + pos + 1
         pages = wl.kvq.make_pages(wl.table, wl.max_pages, wl.n2_dev, wl.n4_before)
         out, lse = _decode32(wl, 0, pos, pages=pages)
         q = wl.q[0][pos].cpu()
         region = wl.cache[lp.offset:lp.offset + lp.bytes].cpu().numpy()
         for r in _requests(wl.B):
+            n2, n4 = wl.n2s[r], wl.P - wl.n2s[r] + pos + 1
             order = wl._prompt_order(r) + list(range(wl.P, wl.P + pos + 1))
             np2, np4 = n2 // 16, -(-n4 // 16)
             compact = np.arange(np2 + np4, dtype=np.int32)  # the oracle's own placement
