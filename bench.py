@@ -67,9 +67,9 @@ WORKLOADS = {
                                        desc="Qwen2.5-7B shape, batch 32, context 8192..8223, seeded "
                                             "9 x K8V4 + 19 x K4V2 (3.96 bits)"),
 }
-# Paged INT2/INT4 pool (TriAxialKV-style): every layer is a pool of 16-token pages; half of
-# each request's prompt tokens, in seeded 32-token runs, are INT2 (keys per-channel, values
-# per-token), the rest and every decoded token INT4 per-token; tables in seeded page order.
+# Paged INT2/INT4 pool (TriAxialKV-style): every layer is a pool of 16-token pages; the prompt
+# tokens of the tags the allocator sets to INT2, in 32-token groups, are INT2 (keys per-channel,
+# values per-token), the rest and every decoded token INT4 per-token; tables in seeded page order.
 PAGED_WORKLOADS = {
     "paged-b16-l32768-int2int4": dict(layers=36, hq=32, hkv=8, batch=16, prefill=32767, cycle=32,
                                       outliers=(4, 10.0), tags=8, budget=3.0,

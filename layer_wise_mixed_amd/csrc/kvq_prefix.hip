@@ -11,15 +11,19 @@
 //   per group  the 512 threads dequantize the record (fmaf(code, scale, zero)
 //              in fp32, KIVI and KVTuner summary pages: asymmetric groupwise
 //              codes; keys per channel or per token, values per token) into
-//              fp16 high and low planes, x = hi + lo with lo = fp16(x - hi),
-//              kept in the record's own lane order: octet o of lane l is the
-//              MFMA operand lane l needs (16x16x32 f16 tiles);
+//              fp16 operands kept in the record's own lane order: octet o of
+//              lane l is the MFMA operand lane l needs (16x16x32 f16 tiles).
+//              Keys as a high and a low plane, x = hi + lo with lo = fp16(x -
+//              hi); values as one plane, rounded to nearest;
 //   scores     S[token][row] = (K_hi.q + K_lo.q) * softmax_scale * log2(e):
-//              q is fp16 already, so two products keep ~22 significant bits;
+//              q is fp16 already, so two products keep ~22 significant bits
+//              (a score's absolute error sets the weights' relative error);
 //   softmax    exp2 of (score - reference max); the reference is raised
 //              (and the sums rescaled) only when a score exceeds it by more
 //              than kSlack, so most groups need no cross-lane max at all;
-//   output     O^T[ch][row] += V^T . P, again hi.hi + hi.lo + lo.hi.
+//   output     O^T[ch][row] += V^T . P with V and P each rounded once to fp16
+//              (nearest): a relative error of about 2^-11 a term, unbiased,
+//              in fp32 sums.
 // The next group's record loads are in flight while the current group is
 // multiplied; its dequantization goes to the second LDS buffer, and one
 // barrier per group separates the two. The fp16 tail is dequantized the same
@@ -55,6 +59,14 @@ __device__ inline void split8(const float* x, h8_t& hi, h8_t& lo) {
   }
 }
 
+// 8 floats rounded to nearest fp16
+__device__ inline h8_t to_h8(const float* x) {
+  h8_t h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)x[i];
+  return h;
+}
+
 __device__ inline float sum_lane_groups(float x) {
   x += __shfl_xor(x, 16);
   x += __shfl_xor(x, 32);
@@ -72,7 +84,7 @@ __device__ inline float max_lane_groups(float x) {
 // octet u holds channel 16u + l%16 for the tokens 16(i/4) + 4(l/16) + i%4,
 // i = 0..7, the order in which the score tile leaves them in each lane.
 struct GroupBuf {
-  h8_t khi[8][64], klo[8][64], vhi[8][64], vlo[8][64];
+  h8_t khi[8][64], klo[8][64], vhi[8][64];
 };
 
 // A thread's share of a record: lane `lane`, key octet w (token
@@ -195,7 +207,7 @@ __device__ __forceinline__ void dequant_share(const Share<KB, VB, KTOK>& sh, Gro
     }
     if constexpr (MASK) x[i] = 16 * (i >> 2) + 4 * a + (i & 3) < ntok ? x[i] : 0.f;
   }
-  split8(x, b.vhi[w][lane], b.vlo[w][lane]);
+  b.vhi[w][lane] = to_h8(x);
 }
 
 struct Acc {
@@ -259,7 +271,7 @@ __device__ __forceinline__ void group_step(const GroupBuf& b, const h8_t (*qv)[4
       acc.m[n] = mnew;
     }
   }
-  h8_t ph[kNT], pl[kNT];
+  h8_t ph[kNT];
 #pragma unroll
   for (int n = 0; n < kNT; ++n) {
     float p[8];
@@ -272,17 +284,13 @@ __device__ __forceinline__ void group_step(const GroupBuf& b, const h8_t (*qv)[4
         p[4 * t + i] = x;
         acc.lpart[n] += x;
       }
-    split8(p, ph[n], pl[n]);
+    ph[n] = to_h8(p);
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const h8_t vh = b.vhi[u][lane], vl = b.vlo[u][lane];
+    const h8_t vh = b.vhi[u][lane];
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) {
-      acc.o[n][u] = mfma(vh, ph[n], acc.o[n][u]);
-      acc.o[n][u] = mfma(vh, pl[n], acc.o[n][u]);
-      acc.o[n][u] = mfma(vl, ph[n], acc.o[n][u]);
-    }
+    for (int n = 0; n < kNT; ++n) acc.o[n][u] = mfma(vh, ph[n], acc.o[n][u]);
   }
 }
 
@@ -429,7 +437,7 @@ __device__ __forceinline__ void dequant_int4_pair(const uint8_t* pa, const uint8
       x[i] = j < ntok ? fmaf(code, vm[mi], vm[64 + mi]) : 0.f;
     }
   }
-  split8(x, b.vhi[w][lane], b.vlo[w][lane]);
+  b.vhi[w][lane] = to_h8(x);
 }
 
 __global__ __launch_bounds__(kWaves * 64, 1) void prefix_paged_kernel(DecodeArgs a) {
@@ -496,8 +504,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void prefix_paged_kernel(DecodeArgs
 // row, which the merge pass joins with the prefix splits by log-sum-exp
 // (TriAxialKV page, "Facts": partial attentions merged by online
 // log-sum-exp). Keys and values are fp16 and q is fp16, so the score products
-// are exact with one fp16 operand each (no low planes); p is split into fp16
-// high and low parts as in the prefix pass.
+// are exact with one fp16 operand each (no low planes); p is rounded to fp16
+// as in the prefix pass.
 
 // Block kb of the chunk's keys and values (tokens 32 kb .. 32 kb + 31; those
 // at or past `chunk` become 0) into the record lane order of GroupBuf.
@@ -562,7 +570,7 @@ __device__ __forceinline__ void chunk_step(const GroupBuf& b, const h8_t (*qv)[4
       acc.m[n] = mnew;
     }
   }
-  h8_t ph[kNT], pl[kNT];
+  h8_t ph[kNT];
 #pragma unroll
   for (int n = 0; n < kNT; ++n) {
     float p[8];
@@ -575,16 +583,13 @@ __device__ __forceinline__ void chunk_step(const GroupBuf& b, const h8_t (*qv)[4
         p[4 * t + i] = x;
         acc.lpart[n] += x;
       }
-    split8(p, ph[n], pl[n]);
+    ph[n] = to_h8(p);
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const h8_t vh = b.vhi[u][lane];
 #pragma unroll
-    for (int n = 0; n < kNT; ++n) {
-      acc.o[n][u] = mfma(vh, ph[n], acc.o[n][u]);
-      acc.o[n][u] = mfma(vh, pl[n], acc.o[n][u]);
-    }
+    for (int n = 0; n < kNT; ++n) acc.o[n][u] = mfma(vh, ph[n], acc.o[n][u]);
   }
 }
 

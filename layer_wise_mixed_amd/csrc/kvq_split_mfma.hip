@@ -293,12 +293,23 @@ __device__ __forceinline__ void group_scores(const uint32_t* kw, const float* km
   }
 }
 
-// Raise the running max to cover a block max; rescale what was accumulated.
+// The softmax reference acc.m only has to bound every score seen so far
+// (weights exp2(score - m) <= 1, the fp16 operand range relies on it): when
+// a block's scores pass it, it moves to the block max plus kHeadroom, so that
+// later blocks rarely pass it again and the accumulators are rescaled (64
+// multiplies) a few times per wave instead of at most groups. The largest
+// weight is then between 2^-kHeadroom and 1, which costs the hi/lo operand
+// split nothing but that many bits of exponent range. Whether anything passed
+// is one vote over each lane's own scores against its column's reference;
+// only then is the column max formed across the four lane groups.
+constexpr float kHeadroom = 3.0f;
+
 __device__ __forceinline__ void raise_max(float bm, Acc& acc) {
-  bm = max_lane_groups(bm);
-  const float mnew = fmaxf(acc.m, bm);
-  if (__any(mnew > acc.m)) {
-    const float alpha = __builtin_amdgcn_exp2f(acc.m - mnew);  // exp2(-inf) = 0 for the first group
+  if (__any(bm > acc.m)) {
+    bm = max_lane_groups(bm);
+    const float mnew = bm > acc.m ? bm + kHeadroom : acc.m;
+    // 0 while nothing is accumulated (acc.m = -inf; also when mnew is)
+    const float alpha = acc.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(acc.m - mnew);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       acc.o[u] *= alpha;

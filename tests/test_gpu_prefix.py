@@ -78,15 +78,24 @@ def test_prefix_matches_oracle(gpu, oq, cases, hq, hkv, chunk, splits):
             raise AssertionError(f"layer {l} {c.cfgs[l]}: {e}") from None
 
 
-def test_splits_agree(gpu, cases):
-    # one split and several give the same rows to within the merge's rounding
+def test_splits_agree(gpu, cases, oq):
+    # one split and several give the same rows to within the operand rounding: the P.V
+    # operands (weight and value) are each rounded once to fp16, at most 2^-11 relative, so
+    # a row's output is within 2^-10 max|v| of exact and two of them within 2^-9 max|v|
+    # (max over the request's dequantized values); the log-sum-exp comes from fp32 sums of
+    # the unrounded weights and agrees to 1e-5
     c = cases[(8, 2)]
     q = chunk_queries(c.seed, 0, c.batch, 8, 200, 9)
     a, la = run_prefix(gpu, c, 0, q, 1)
     b, lb = run_prefix(gpu, c, 0, q, 4)
-    full = [r for r, L in enumerate(c.lens) if L > 0]
-    np.testing.assert_allclose(b[full], a[full], rtol=0, atol=1e-5)
-    np.testing.assert_allclose(lb[full], la[full], rtol=0, atol=1e-5)
+    kb, vb, ka, _ = c.cfgs[0]
+    for r, L in enumerate(c.lens):
+        if L == 0:
+            continue
+        vmax = max(np.abs(oq.dequant_stream(oq.quantize_stream(c.k[0][r, h, :L].numpy(), c.v[0][r, h, :L].numpy(),
+                                                               kb, vb, ka == 1))[1]).max() for h in range(c.hkv))
+        np.testing.assert_allclose(b[r], a[r], rtol=0, atol=2.0 ** -9 * vmax)
+        np.testing.assert_allclose(lb[r], la[r], rtol=0, atol=1e-5)
 
 
 def test_merged_with_chunk_part_is_chunked_prefill(gpu, oq, cases):
