@@ -38,7 +38,7 @@ constexpr int CS = D + 4;
 // scale/zero. The elements are visited from position rot on (mod 32): a lane
 // that starts elsewhere than its neighbours reads another LDS bank (the
 // result does not depend on the order).
-__device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint8_t* codes,
+__device__ __forceinline__ void quantize32(const uint16_t* x, int stride, int bits, uint8_t* codes,
                                   int cstride, float* scale, float* zero, int rot = 0) {
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll 8
@@ -51,17 +51,33 @@ __device__ inline void quantize32(const uint16_t* x, int stride, int bits, uint8
   const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
   *scale = s;
   *zero = mn;
+  if (s == 0.0f) {
+#pragma unroll 8
+    for (int i = 0; i < GS; ++i) codes[((i + rot) & (GS - 1)) * cstride] = 0;
+    return;
+  }
+  // The code is rint of the correctly rounded quotient Q = RN(t / scale),
+  // t = x - zero. q = RN(t RN(1 / scale)) differs from t / scale by at most
+  // 2^-23 relative (two roundings) and Q by 2^-24 more: below 1.5 * 2^-23 *
+  // 255 < 2^-14 for every quotient up to 255. So rint(q) = rint(Q) unless q
+  // lies within 2^-14 of a half-integer; those elements are marked and
+  // recoded with the IEEE division after the loop (a fraction of a percent
+  // of fp16 inputs, exact ties included).
+  const float y = __fdiv_rn(1.0f, s);
+  uint32_t redo = 0;
 #pragma unroll 8
   for (int i = 0; i < GS; ++i) {
     const int k = (i + rot) & (GS - 1);
-    uint8_t code = 0;
-    if (s != 0.0f) {
-      const float t = __fdiv_rn(__fsub_rn(h2f(x[k * stride]), mn), s);
-      float r = rintf(t);
-      r = fminf(fmaxf(r, 0.0f), levels);
-      code = (uint8_t)r;
-    }
-    codes[k * cstride] = code;
+    // (t = x - zero >= 0, so q >= 0 and only the top needs clamping)
+    const float q = __fmul_rn(__fsub_rn(h2f(x[k * stride]), mn), y);
+    redo |= fabsf(__fsub_rn(__builtin_amdgcn_fractf(q), 0.5f)) < 0x1p-14f ? 1u << k : 0u;
+    codes[k * cstride] = (uint8_t)fminf(rintf(q), levels);
+  }
+  while (redo != 0) {
+    const int k = __builtin_ctz(redo);
+    redo &= redo - 1;
+    const float q = __fdiv_rn(__fsub_rn(h2f(x[k * stride]), mn), s);
+    codes[k * cstride] = (uint8_t)fminf(fmaxf(rintf(q), 0.0f), levels);
   }
 }
 
@@ -102,7 +118,7 @@ __device__ inline void pack_block_bits(uint8_t* blk, int bits, const uint16_t (*
 // write its record; cs is LDS scratch for the codes. 256 threads. A
 // per-token group (row j) starts at position 2j: the 16 rows a wave covers
 // then read 16 different banks.
-__device__ inline void quantize_record(const uint16_t (*xs)[GS][D], uint8_t (*cs)[GS][CS], uint8_t* rec, int kb,
+__device__ __forceinline__ void quantize_record(const uint16_t (*xs)[GS][D], uint8_t (*cs)[GS][CS], uint8_t* rec, int kb,
                                        int vb, int k_token, int tid) {
   const RecordParts parts = record_parts(kb, vb);
   float* kmeta = (float*)(rec + parts.kmeta);
