@@ -34,50 +34,168 @@ __device__ inline void tail_put(uint8_t* rec, bool is_v, int j, int c, uint16_t 
 // rows at once spread over the LDS banks.
 constexpr int CS = D + 4;
 
-// One group of 32 values x[i * stride]; writes codes[i * cstride], returns
-// scale/zero. The elements are visited from position rot on (mod 32): a lane
-// that starts elsewhere than its neighbours reads another LDS bank (the
-// result does not depend on the order).
-__device__ __forceinline__ void quantize32(const uint16_t* x, int stride, int bits, uint8_t* codes,
-                                  int cstride, float* scale, float* zero, int rot = 0) {
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll 8
-  for (int i = 0; i < GS; ++i) {
-    const float v = h2f(x[((i + rot) & (GS - 1)) * stride]);
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+// Minimum and maximum of 32 fp16 values held two a word, on packed fp16
+// (exact: fp16 min and max lose nothing, and the order does not matter).
+__device__ __forceinline__ void minmax32(const uint32_t (&w)[16], float* mn, float* mx) {
+  const uint32_t w0 = w[0];  // (each word copied to a scalar before the cast)
+  h2_t lo = __builtin_bit_cast(h2_t, w0), hi = lo;
+#pragma unroll
+  for (int d = 1; d < 16; ++d) {
+    const uint32_t u = w[d];
+    const h2_t v = __builtin_bit_cast(h2_t, u);
+    lo = __builtin_elementwise_minimum(lo, v);
+    hi = __builtin_elementwise_maximum(hi, v);
   }
+  *mn = fminf((float)lo[0], (float)lo[1]);
+  *mx = fmaxf((float)hi[0], (float)hi[1]);
+}
+
+// The code is rint of the correctly rounded quotient Q = RN(t / scale),
+// t = RN(x - zero). q = RN(t RN(1 / scale)) differs from t / scale by at most
+// 2^-23 relative (two roundings) and Q by 2^-24 more: below 1.5 * 2^-23 *
+// 255 < 2^-14 for every quotient up to 255, so rint(q) = rint(Q) unless q
+// lies within 2^-14 of a half-integer. code_fast returns rint(q) and the
+// distance d of t RN(1 / scale) from it (within 2^-17 of |q - rint(q)|); a
+// value with d > 1/2 - 2^-14 is recoded with the IEEE division (a fraction of
+// a percent of fp16 inputs, exact ties included). No clamp is needed on the
+// fast path: t <= RN(max - min) and y = RN(1 / scale) put q below
+// levels (1 + 2^-22) < levels + 1/2, and t >= 0.
+constexpr float kNear = 0.5f - 0x1p-14f;
+
+__device__ __forceinline__ float code_fast(uint16_t h, float mn, float y, float* d) {
+  const float t = __fsub_rn(h2f(h), mn);
+  const float r = rintf(__fmul_rn(t, y));
+  *d = fabsf(__builtin_fmaf(t, y, -r));
+  return r;
+}
+
+__device__ __forceinline__ uint8_t code_exact(uint16_t h, float mn, float s, float levels) {
+  const float q = __fdiv_rn(__fsub_rn(h2f(h), mn), s);
+  return (uint8_t)fminf(fmaxf(rintf(q), 0.0f), levels);
+}
+
+// One per-token group: the 32 fp16 values row[0..31] (LDS, 16-byte aligned)
+// to codes crow[0..31] (LDS, 4-byte aligned); returns scale/zero. The values
+// are read as four 16-byte pieces starting with piece rot & 3 (callers spread
+// the lanes of a wave over the LDS banks with it), held in registers for both
+// passes; the codes are packed four a word before they are stored.
+__device__ __forceinline__ void quantize_token32(const uint16_t* row, int rot, int bits, uint8_t* crow,
+                                                 float* scale, float* zero) {
+  typedef uint32_t w4_t __attribute__((ext_vector_type(4)));
+  w4_t x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = *(const w4_t*)(row + 8 * ((i + rot) & 3));
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = x[i >> 2][i & 3];
+  float mn, mx;
+  minmax32(w, &mn, &mx);
   const float levels = (float)((1 << bits) - 1);
   const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
   *scale = s;
   *zero = mn;
   if (s == 0.0f) {
-#pragma unroll 8
-    for (int i = 0; i < GS; ++i) codes[((i + rot) & (GS - 1)) * cstride] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(uint32_t*)(crow + 4 * i) = 0u;
     return;
   }
-  // The code is rint of the correctly rounded quotient Q = RN(t / scale),
-  // t = x - zero. q = RN(t RN(1 / scale)) differs from t / scale by at most
-  // 2^-23 relative (two roundings) and Q by 2^-24 more: below 1.5 * 2^-23 *
-  // 255 < 2^-14 for every quotient up to 255. So rint(q) = rint(Q) unless q
-  // lies within 2^-14 of a half-integer; those elements are marked and
-  // recoded with the IEEE division after the loop (a fraction of a percent
-  // of fp16 inputs, exact ties included).
   const float y = __fdiv_rn(1.0f, s);
-  uint32_t redo = 0;
-#pragma unroll 8
-  for (int i = 0; i < GS; ++i) {
-    const int k = (i + rot) & (GS - 1);
-    // (t = x - zero >= 0, so q >= 0 and only the top needs clamping)
-    const float q = __fmul_rn(__fsub_rn(h2f(x[k * stride]), mn), y);
-    redo |= fabsf(__fsub_rn(__builtin_amdgcn_fractf(q), 0.5f)) < 0x1p-14f ? 1u << k : 0u;
-    codes[k * cstride] = (uint8_t)fminf(rintf(q), levels);
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float d;
+      const float r = code_fast((uint16_t)(w[4 * i + (k >> 1)] >> (16 * (k & 1))), mn, y, &d);
+      dmax = fmaxf(dmax, d);
+      c[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r, k & 3, c[k >> 2]);
+    }
+    uint8_t* dst = crow + 8 * ((i + rot) & 3);
+    *(uint32_t*)dst = c[0];
+    *(uint32_t*)(dst + 4) = c[1];
   }
-  while (redo != 0) {
-    const int k = __builtin_ctz(redo);
-    redo &= redo - 1;
-    const float q = __fdiv_rn(__fsub_rn(h2f(x[k * stride]), mn), s);
-    codes[k * cstride] = (uint8_t)fminf(fmaxf(rintf(q), 0.0f), levels);
+  if (dmax > kNear) {  // rare: recode the values near a rounding boundary
+#pragma unroll 1
+    for (int k = 0; k < GS; ++k) {
+      float d;
+      (void)code_fast(row[k], mn, y, &d);
+      if (d > kNear) crow[k] = code_exact(row[k], mn, s, levels);
+    }
+  }
+}
+
+// The value of lane l ^ 32 (h: 1 in lanes 32..63). v_permlane32_swap trades
+// lanes 32..63 of its first operand with lanes 0..31 of its second.
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x, int h) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const uint32_t a = r[0], b = r[1];
+  return h ? a : b;
+}
+
+// Two per-channel groups, channels c0 and c0 + 1, by lanes l and l ^ 32 of
+// one wave (h = l >> 5; the whole wave must call): lane h reads the channel
+// pair at rows 2i + h (i < 16) as one 32-bit word (pair: &x[h][c0], row
+// stride D, LDS), the two lanes combine their minima and maxima, lane h
+// computes the scale of channel c0 + h (returned with its zero), and each
+// lane codes its 16 rows of both channels, two codes a 16-bit store (cpair:
+// &codes[h][c0], row stride CS).
+__device__ __forceinline__ void quantize_channel_pair(const uint16_t* pair, int h, int bits, uint8_t* cpair,
+                                                      float* scale, float* zero) {
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = *(const uint32_t*)(pair + 2 * i * D);
+  const uint32_t w0 = w[0];
+  h2_t lo = __builtin_bit_cast(h2_t, w0), hi = lo;
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    const uint32_t u = w[i];
+    const h2_t v = __builtin_bit_cast(h2_t, u);
+    lo = __builtin_elementwise_minimum(lo, v);
+    hi = __builtin_elementwise_maximum(hi, v);
+  }
+  {
+    const uint32_t ul = __builtin_bit_cast(uint32_t, lo), uh = __builtin_bit_cast(uint32_t, hi);
+    const uint32_t pl = lane_xor32(ul, h), ph = lane_xor32(uh, h);
+    lo = __builtin_elementwise_minimum(lo, __builtin_bit_cast(h2_t, pl));
+    hi = __builtin_elementwise_maximum(hi, __builtin_bit_cast(h2_t, ph));
+  }
+  const float mn0 = (float)lo[0], mn1 = (float)lo[1];
+  const float mn = h ? mn1 : mn0, mx = h ? (float)hi[1] : (float)hi[0];
+  const float levels = (float)((1 << bits) - 1);
+  const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
+  *scale = s;
+  *zero = mn;
+  // a constant group (s = 0) takes y = 0: every t is 0 there, so every code 0
+  const float y = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+  const float yp = __builtin_bit_cast(float, lane_xor32(__builtin_bit_cast(uint32_t, y), h));
+  const float y0 = h ? yp : y, y1 = h ? y : yp;
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t u = w[i];
+    float d0, d1;
+    const float r0 = code_fast((uint16_t)u, mn0, y0, &d0);
+    const float r1 = code_fast((uint16_t)(u >> 16), mn1, y1, &d1);
+    dmax = fmaxf(dmax, fmaxf(d0, d1));
+    const uint32_t c = __builtin_amdgcn_cvt_pk_u8_f32(r1, 1, __builtin_amdgcn_cvt_pk_u8_f32(r0, 0, 0u));
+    *(uint16_t*)(cpair + 2 * i * CS) = (uint16_t)c;
+  }
+  const float sp = __builtin_bit_cast(float, lane_xor32(__builtin_bit_cast(uint32_t, s), h));
+  if (dmax > kNear) {  // rare: recode the values near a rounding boundary
+    const float s0 = h ? sp : s, s1 = h ? s : sp;
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint16_t x = pair[2 * i * D + e];
+        float d;
+        (void)code_fast(x, e ? mn1 : mn0, e ? y1 : y0, &d);
+        if (d > kNear) cpair[2 * i * CS + e] = code_exact(x, e ? mn1 : mn0, e ? s1 : s0, levels);
+      }
+    }
   }
 }
 
@@ -115,9 +233,10 @@ __device__ inline void pack_block_bits(uint8_t* blk, int bits, const uint16_t (*
 }
 
 // Quantize one full 32-token group (xs: fp16 K and V [32][128], in LDS) and
-// write its record; cs is LDS scratch for the codes. 256 threads. A
-// per-token group (row j) starts at position 2j: the 16 rows a wave covers
-// then read 16 different banks.
+// write its record; cs is LDS scratch for the codes (4-byte aligned). 256
+// threads. The per-token group (row j, channels 32n ..) starts at piece
+// j + 2 (n >> 1): the 16-byte reads of a wave's 64 groups then fall on
+// distinct LDS banks.
 __device__ __forceinline__ void quantize_record(const uint16_t (*xs)[GS][D], uint8_t (*cs)[GS][CS], uint8_t* rec, int kb,
                                        int vb, int k_token, int tid) {
   const RecordParts parts = record_parts(kb, vb);
@@ -127,15 +246,16 @@ __device__ __forceinline__ void quantize_record(const uint16_t (*xs)[GS][D], uin
     if (kb == 16) {
       // the fp16 values are packed as they are, straight from xs
     } else if (!k_token) {
-      const int c = tid;
+      // channel pair 2 p, 2 p + 1 by lanes l and l ^ 32 of wave tid / 64
+      const int h = (tid >> 5) & 1, p = ((tid >> 6) << 5) | (tid & 31), c = 2 * p + h;
       float s, z;
-      quantize32(&xs[0][0][c], D, kb, &cs[0][0][c], CS, &s, &z);
+      quantize_channel_pair(&xs[0][h][2 * p], h, kb, &cs[0][h][2 * p], &s, &z);
       kmeta[meta_channel(c)] = s;
       kmeta[128 + meta_channel(c)] = z;
     } else {
       const int j = tid >> 2, n = tid & 3;
       float s, z;
-      quantize32(&xs[0][j][32 * n], 1, kb, &cs[0][j][32 * n], 1, &s, &z, 2 * j);
+      quantize_token32(&xs[0][j][32 * n], j + 2 * (n >> 1), kb, &cs[0][j][32 * n], &s, &z);
       kmeta[meta_token(j, n)] = s;
       kmeta[128 + meta_token(j, n)] = z;
     }
@@ -146,7 +266,7 @@ __device__ __forceinline__ void quantize_record(const uint16_t (*xs)[GS][D], uin
     } else {
       const int j = t2 >> 2, n = t2 & 3;
       float s, z;
-      quantize32(&xs[1][j][32 * n], 1, vb, &cs[1][j][32 * n], 1, &s, &z, 2 * j);
+      quantize_token32(&xs[1][j][32 * n], j + 2 * (n >> 1), vb, &cs[1][j][32 * n], &s, &z);
       vmeta[meta_token(j, n)] = s;
       vmeta[128 + meta_token(j, n)] = z;
     }
@@ -168,7 +288,7 @@ __device__ inline void page_append_int4(uint8_t* page, const uint16_t (*xs)[GS][
     const int tensor = tid >> 6, p = (tid >> 2) & 15, n = tid & 3;
     if (p >= p_lo && p < p_hi) {
       float s, z;
-      quantize32(&xs[tensor][p][32 * n], 1, 4, &cs[tensor][p][32 * n], 1, &s, &z, 2 * p);
+      quantize_token32(&xs[tensor][p][32 * n], p + 2 * (n >> 1), 4, &cs[tensor][p][32 * n], &s, &z);
       float* meta = (float*)(page + (tensor ? INT4_VMETA : INT4_KMETA));
       meta[16 * n + p] = s;
       meta[64 + 16 * n + p] = z;

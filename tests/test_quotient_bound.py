@@ -1,9 +1,11 @@
 """The append kernel's quantizer forms each code from q = RN(t RN(1/s)) instead of the IEEE
-quotient Q = RN(t/s), and recodes an element with the IEEE division only when q lies within
-2^-14 of a half-integer. This checks, in float32 arithmetic on the CPU (numpy rounds every
-float32 operation to nearest), the bound that makes this exact: |q - Q| < 2^-14 for all
-quotients up to 255 -- so wherever rint(q) and rint(Q) differ the element is flagged -- over
-groups shaped like the quantizer's (t = x - min >= 0, s = (max - min) / (2^b - 1))."""
+quotient Q = RN(t/s), and recodes an element with the IEEE division only when the distance
+d = |RN(t y - rint(q))| (y = RN(1/s); one fused multiply-add) exceeds 1/2 - 2^-14. This checks,
+in float32 arithmetic on the CPU (numpy rounds every float32 operation to nearest; the fused
+operation is formed exactly in float64 and rounded once), the bound that makes this exact:
+|q - Q| < 2^-14 for all quotients up to 255, and every element where rint(q) and rint(Q)
+differ is flagged -- over groups shaped like the quantizer's (t = x - min >= 0,
+s = (max - min) / (2^b - 1)). The fast codes never exceed 2^b - 1, so they need no clamp."""
 import numpy as np
 
 
@@ -25,9 +27,13 @@ def test_fast_quotient_within_bound_and_flags_every_difference():
         Q = t / s
         assert q.dtype == np.float32 and Q.dtype == np.float32
         assert np.all(np.abs(q.astype(np.float64) - Q.astype(np.float64)) < 2.0 ** -14)
-        flagged = np.abs((q - np.floor(q)) - np.float32(0.5)) < np.float32(2.0 ** -14)
-        differ = np.rint(q) != np.rint(Q)
+        r = np.rint(q)
+        d = np.abs((t.astype(np.float64) * y.astype(np.float64) - r).astype(np.float32))
+        flagged = d > np.float32(0.5) - np.float32(2.0 ** -14)
+        differ = r != np.rint(Q)
+        assert np.any(flagged)
         assert not np.any(differ & ~flagged)
+        assert r.max() <= (1 << bits) - 1 and r.min() >= 0
 
 
 def test_exact_half_quotients_are_flagged():
@@ -36,5 +42,7 @@ def test_exact_half_quotients_are_flagged():
         s = np.float32(0.25)
         k = np.arange(levels, dtype=np.float32)
         t = (k + np.float32(0.5)) * s
-        q = t * (np.float32(1.0) / s)
-        assert np.all(np.abs((q - np.floor(q)) - np.float32(0.5)) < np.float32(2.0 ** -14))
+        y = np.float32(1.0) / s
+        q = t * y
+        d = np.abs((t.astype(np.float64) * np.float64(y) - np.rint(q)).astype(np.float32))
+        assert np.all(d > np.float32(0.5) - np.float32(2.0 ** -14))
