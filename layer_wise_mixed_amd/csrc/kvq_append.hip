@@ -12,17 +12,21 @@
 namespace kvq {
 namespace {
 
-// One workgroup per (x, stream); it completes the x-th of gridDim.x runs of
-// consecutive groups of this call, and while one group is quantized the fp16
-// rows of its next whole-new group are already loading (in registers), so
-// that the stream of loads does not stop for the arithmetic.
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+// One workgroup of two waves per (x, stream, tensor): it completes the
+// tensor's part (keys for blockIdx.z = 0, values for 1) of the x-th of
+// gridDim.x runs of consecutive groups of this call; keys and values of one
+// group are quantized by different workgroups that never wait on each other.
+// While one group is quantized the fp16 rows of its next whole-new group are
+// already loading (in registers), so that the stream of loads does not stop
+// for the arithmetic.
+__global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][GS][D];
-  __shared__ __attribute__((aligned(16))) uint8_t cs[2][GS][CS];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[GS][D];
+  __shared__ __attribute__((aligned(16))) uint8_t cs[GS][CS];
   const LayerGeom& g = a.geo;
   const int tid = threadIdx.x;
   const int sigma = blockIdx.y;
+  const int is_v = blockIdx.z;
   const int r = sigma / g.hkv;
   const int L0 = a.seq_lens[r];
   const int L1 = L0 + a.n_new;
@@ -31,21 +35,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int F = L1 / GS - m0;  // groups this call completes
   uint8_t* stream = g.base + (size_t)sigma * g.stream_bytes;
   uint8_t* tail = stream + g.tail_offset;
-  const uint16_t* kn = a.k_new + (size_t)sigma * a.n_new * D;
-  const uint16_t* vn = a.v_new + (size_t)sigma * a.n_new * D;
+  const uint16_t* src = (is_v ? a.v_new : a.k_new) + (size_t)sigma * a.n_new * D;
 
-  // a whole-new group's 32 contiguous rows of k_new and of v_new, 8 KiB each,
-  // two 16-byte pieces a thread and tensor
-  constexpr int kPer = GS * D / 8 / 256;
-  u4_t ka[kPer], va[kPer];
+  // a whole-new group's 32 contiguous rows of this tensor, 8 KiB: four
+  // 16-byte pieces a thread
+  constexpr int kPer = GS * D / 8 / 128;
+  u4_t xa[kPer];
   auto fetch = [&](int y) {
-    const u4_t* ks = (const u4_t*)(kn + (size_t)(GS * (m0 + y) - L0) * D);
-    const u4_t* vs = (const u4_t*)(vn + (size_t)(GS * (m0 + y) - L0) * D);
+    const u4_t* xsrc = (const u4_t*)(src + (size_t)(GS * (m0 + y) - L0) * D);
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      ka[q] = ks[tid + 256 * q];
-      va[q] = vs[tid + 256 * q];
-    }
+    for (int q = 0; q < kPer; ++q) xa[q] = xsrc[tid + 128 * q];
   };
   auto whole_new = [&](int y) { return GS * (m0 + y) >= L0; };
 
@@ -57,29 +56,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int m = m0 + y;
     if (whole_new(y)) {
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        ((u4_t*)&xs[0][0][0])[tid + 256 * q] = ka[q];
-        ((u4_t*)&xs[1][0][0])[tid + 256 * q] = va[q];
-      }
+      for (int q = 0; q < kPer; ++q) ((u4_t*)&xs[0][0])[tid + 128 * q] = xa[q];
     } else {
+#pragma unroll 1
       for (int idx = tid; idx < GS * D; idx += blockDim.x) {
         const int i = idx >> 7, c = idx & 127;
         const int t = GS * m + i;
-        uint16_t kv, vv;
-        if (t < L0) {  // earlier tokens of this group wait in the tail
-          kv = tail_get(tail, false, i, c);
-          vv = tail_get(tail, true, i, c);
-        } else {
-          kv = kn[(size_t)(t - L0) * D + c];
-          vv = vn[(size_t)(t - L0) * D + c];
-        }
-        xs[0][i][c] = kv;
-        xs[1][i][c] = vv;
+        // earlier tokens of this group wait in the tail
+        xs[i][c] = t < L0 ? tail_get(tail, is_v, i, c) : src[(size_t)(t - L0) * D + c];
       }
     }
     __syncthreads();
     if (y + 1 < yend && whole_new(y + 1)) fetch(y + 1);  // in flight during the quantization
-    quantize_record(xs, cs, stream + (size_t)m * g.record_bytes, g.kb, g.vb, g.k_token, tid);
+    quantize_tensor(xs, cs, stream + (size_t)m * g.record_bytes, is_v, g.kb, g.vb, g.k_token, tid);
     __syncthreads();  // the next group rewrites xs and cs
   }
   if (blockIdx.x == 0) {  // after its flush (if any) has read the old tail slots
@@ -87,9 +76,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int nt = L1 - tstart;
     for (int idx = tid; idx < nt * D; idx += blockDim.x) {
       const int t = tstart + (idx >> 7), c = idx & 127;
-      const int slot = t % GS;
-      tail_put(tail, false, slot, c, kn[(size_t)(t - L0) * D + c]);
-      tail_put(tail, true, slot, c, vn[(size_t)(t - L0) * D + c]);
+      tail_put(tail, is_v, t % GS, c, src[(size_t)(t - L0) * D + c]);
     }
   }
 }
@@ -248,20 +235,23 @@ hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s) 
   return hipGetLastError();
 }
 
+// (run, stream) workgroups per tensor of a long append: two rounds of the
+// 10 two-wave workgroups a CU holds (registers), over 256 CUs and two tensors
+constexpr int kAppendRuns = 2560;
+
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev) {
   const int y = a.n_new > 0 ? (a.n_new + GS - 1) / GS : 0;
   if (y == 0 || batch == 0) return hipSuccess;
-  // long appends (prefill): two rounds of workgroups (6 fit a CU by their
-  // LDS, 256 CUs), each looping over a run of its stream's groups (one round
-  // measured up to 7% slower, a workgroup per group up to 40% slower); short
-  // ones: a workgroup per group
+  // long appends (prefill): about kAppendRuns (run, stream) workgroups per
+  // tensor, each looping over a run of its stream's groups; short ones: a
+  // workgroup per group
   const int streams = batch * a.geo.hkv;
   int x = y;
   if (y > 8) {
-    x = (3072 + streams - 1) / streams;
+    x = (kAppendRuns + streams - 1) / streams;
     if (x > y) x = y;
   }
-  return launch_timed(append_kernel, dim3(x, streams), dim3(256), s, ev, a);
+  return launch_timed(append_kernel, dim3(x, streams, 2), dim3(128), s, ev, a);
 }
 
 hipError_t launch_dequant(const DequantArgs& a, int batch, hipStream_t s) {

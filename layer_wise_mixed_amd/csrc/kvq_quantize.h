@@ -199,16 +199,33 @@ __device__ __forceinline__ void quantize_channel_pair(const uint16_t* pair, int 
   }
 }
 
+// Word W = tid + NT k of a code block (NT = 128 or 256 threads, tid < NT):
+// its lane, (W mod 256) / 4, and its word index in that lane, 4 (W / 256) +
+// W mod 4, written so that the compiler sees them as per-thread bases plus
+// constants.
+__device__ __forceinline__ void word_of(int tid, int k, int NT, int* lane, int* w) {
+  if (NT == 128) {
+    *lane = (tid >> 2) + 32 * (k & 1);
+    *w = 4 * (k >> 1) + (tid & 3);
+  } else {
+    *lane = tid >> 2;
+    *w = 4 * k + (tid & 3);
+  }
+}
+
 // Write the 512*BITS bytes of a code block from src[32][ROW] (token,
 // channel): the codes (BITS <= 8, uint8 rows of the staging) or the fp16
 // values themselves (BITS = 16).
-template <int BITS, bool IS_V, class T, int ROW>
-__device__ inline void pack_block(uint8_t* blk, const T (*src)[ROW], int tid, int nthreads) {
+template <int BITS, bool IS_V, int NT, class T, int ROW>
+__device__ inline void pack_block(uint8_t* blk, const T (*src)[ROW], int tid) {
   constexpr int per_word = 32 / BITS;
   constexpr int nwords = 128 * BITS;
-  for (int W = tid; W < nwords; W += nthreads) {
-    const int lane = (W & 255) >> 2;
-    const int w = (W >> 8) * 4 + (W & 3);
+  static_assert(nwords % NT == 0, "whole words a thread");
+#pragma unroll 1
+  for (int k = 0; k < nwords / NT; ++k) {
+    const int W = tid + NT * k;
+    int lane, w;
+    word_of(tid, k, NT, &lane, &w);
     uint32_t word = 0;
 #pragma unroll
     for (int p = 0; p < per_word; ++p) {
@@ -221,14 +238,64 @@ __device__ inline void pack_block(uint8_t* blk, const T (*src)[ROW], int tid, in
   }
 }
 
-template <bool IS_V>
+// The key code block (BITS = 2, 4 or 8) from the staged codes c[32][CS]
+// (token, channel). A key word holds codes of consecutive channels of one
+// token (8 for 4 bits; two runs of 8 for 2 bits; 4 for 8 bits), read as
+// 32-bit words and moved into place with shifts and byte permutes instead
+// of one LDS read a code.
+template <int BITS, int NT>
+__device__ inline void pack_key_codes(uint8_t* blk, const uint8_t (*c)[CS], int tid) {
+  constexpr int nwords = 128 * BITS;
+  static_assert(nwords % NT == 0, "whole words a thread");
+#pragma unroll
+  for (int k = 0; k < nwords / NT; ++k) {
+    const int W = tid + NT * k;
+    int lane, w;
+    word_of(tid, k, NT, &lane, &w);
+    const int a = lane >> 4, r = lane & 15;
+    uint32_t word;
+    if constexpr (BITS == 8) {
+      // codes p = 0..3 of channels c0 + p go to bytes 0, 2, 1, 3
+      const uint32_t d = *(const uint32_t*)&c[16 * (w >> 3) + r][32 * ((w >> 1) & 3) + 8 * a + 4 * (w & 1)];
+      word = __builtin_amdgcn_perm(d, d, 0x03010200u);
+    } else if constexpr (BITS == 4) {
+      // codes p = 0..7: even p to nibbles 0..3, odd p to nibbles 4..7
+      const uint8_t* src = &c[16 * (w >> 2) + r][32 * (w & 3) + 8 * a];
+      const uint32_t d0 = *(const uint32_t*)src, d1 = *(const uint32_t*)(src + 4);
+      const uint32_t f0 = d0 | d0 >> 12, f1 = d1 | d1 >> 12;  // bytes 0, 1: (p0 p2), (p1 p3) and (p4 p6), (p5 p7)
+      word = __builtin_amdgcn_perm(f1, f0, 0x05010400u);
+    } else {
+      // codes p = 0..15 (channels of run p >> 3): even p to bits 0..15 in
+      // pairs, odd p to bits 16..31
+      const uint8_t* ra = &c[16 * (w >> 1) + r][32 * ((2 * w) & 3) + 8 * a];
+      const uint8_t* rb = &c[16 * (w >> 1) + r][32 * ((2 * w + 1) & 3) + 8 * a];
+      const uint32_t x = *(const uint32_t*)ra | *(const uint32_t*)(ra + 4) << 4;
+      const uint32_t z = *(const uint32_t*)rb | *(const uint32_t*)(rb + 4) << 4;
+      const uint32_t y0 = x | x >> 14, y1 = z | z >> 14;  // byte 0: even codes, byte 1: odd codes
+      word = __builtin_amdgcn_perm(y1, y0, 0x05010400u);
+    }
+    *(uint32_t*)(blk + (size_t)W * 4) = word;
+  }
+}
+
+// NT threads (128 or 256), tid < NT.
+template <bool IS_V, int NT>
 __device__ inline void pack_block_bits(uint8_t* blk, int bits, const uint16_t (*xs)[D], const uint8_t (*cs)[CS],
-                                       int tid, int nthreads) {
-  switch (bits) {
-    case 2: pack_block<2, IS_V>(blk, cs, tid, nthreads); break;
-    case 4: pack_block<4, IS_V>(blk, cs, tid, nthreads); break;
-    case 8: pack_block<8, IS_V>(blk, cs, tid, nthreads); break;
-    default: pack_block<16, IS_V>(blk, xs, tid, nthreads); break;
+                                       int tid) {
+  if constexpr (IS_V) {
+    switch (bits) {
+      case 2: pack_block<2, true, NT>(blk, cs, tid); break;
+      case 4: pack_block<4, true, NT>(blk, cs, tid); break;
+      case 8: pack_block<8, true, NT>(blk, cs, tid); break;
+      default: pack_block<16, true, NT>(blk, xs, tid); break;
+    }
+  } else {
+    switch (bits) {
+      case 2: pack_key_codes<2, NT>(blk, cs, tid); break;
+      case 4: pack_key_codes<4, NT>(blk, cs, tid); break;
+      case 8: pack_key_codes<8, NT>(blk, cs, tid); break;
+      default: pack_block<16, false, NT>(blk, xs, tid); break;
+    }
   }
 }
 
@@ -272,8 +339,37 @@ __device__ __forceinline__ void quantize_record(const uint16_t (*xs)[GS][D], uin
     }
   }
   __syncthreads();
-  pack_block_bits<false>(rec, kb, xs[0], cs[0], tid, blockDim.x);
-  pack_block_bits<true>(rec + parts.vcode, vb, xs[1], cs[1], tid, blockDim.x);
+  pack_block_bits<false, 256>(rec, kb, xs[0], cs[0], tid);
+  pack_block_bits<true, 256>(rec + parts.vcode, vb, xs[1], cs[1], tid);
+}
+
+// Quantize and pack one tensor (keys: is_v = 0, values: 1) of a full
+// 32-token group (x: its fp16 rows [32][128], in LDS) into the record; c is
+// LDS scratch for the codes (4-byte aligned). 128 threads (two waves), all of
+// which must call; the same group split as quantize_record: per-channel keys
+// by lane pairs, per-token groups one a thread.
+__device__ __forceinline__ void quantize_tensor(const uint16_t (*x)[D], uint8_t (*c)[CS], uint8_t* rec, int is_v,
+                                                int kb, int vb, int k_token, int tid) {
+  const RecordParts parts = record_parts(kb, vb);
+  const int bits = is_v ? vb : kb;
+  if (bits < 16) {
+    float* meta = (float*)(rec + (is_v ? parts.vmeta : parts.kmeta));
+    float s, z;
+    if (!is_v && !k_token) {
+      const int h = (tid >> 5) & 1, p = ((tid >> 6) << 5) | (tid & 31), ch = 2 * p + h;
+      quantize_channel_pair(&x[h][2 * p], h, bits, &c[h][2 * p], &s, &z);
+      meta[meta_channel(ch)] = s;
+      meta[128 + meta_channel(ch)] = z;
+    } else {
+      const int j = tid >> 2, n = tid & 3;
+      quantize_token32(&x[j][32 * n], j + 2 * (n >> 1), bits, &c[j][32 * n], &s, &z);
+      meta[meta_token(j, n)] = s;
+      meta[128 + meta_token(j, n)] = z;
+    }
+  }
+  __syncthreads();
+  if (is_v) pack_block_bits<true, 128>(rec + parts.vcode, bits, x, c, tid);
+  else pack_block_bits<false, 128>(rec, bits, x, c, tid);
 }
 
 // Write slots p_lo .. p_hi - 1 of one KV head's share of an INT4 page (keys
