@@ -64,11 +64,32 @@ __device__ __forceinline__ void minmax32(const uint32_t (&w)[16], float* mn, flo
 // levels (1 + 2^-22) < levels + 1/2, and t >= 0.
 constexpr float kNear = 0.5f - 0x1p-14f;
 
-__device__ __forceinline__ float code_fast(uint16_t h, float mn, float y, float* d) {
-  const float t = __fsub_rn(h2f(h), mn);
+__device__ __forceinline__ float code_of_t(float t, float y, float* d) {
   const float r = rintf(__fmul_rn(t, y));
   *d = fabsf(__builtin_fmaf(t, y, -r));
   return r;
+}
+
+__device__ __forceinline__ float code_fast(uint16_t h, float mn, float y, float* d) {
+  return code_of_t(__fsub_rn(h2f(h), mn), y, d);
+}
+
+// t = RN(x - mn) for the fp16 value x in half HI of w, as one mixed-precision
+// fma (x * 1 - mn with the fp16 operand widened exactly, one rounding): the
+// same value as converting x and subtracting.
+template <int HI>
+__device__ __forceinline__ float sub_half(uint32_t w, float mn) {
+  float t;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(t) : "v"(w), "v"(mn));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(t) : "v"(w), "v"(mn));
+  return t;
+}
+
+template <int HI>
+__device__ __forceinline__ float code_half(uint32_t w, float mn, float y, float* d) {
+  return code_of_t(sub_half<HI>(w, mn), y, d);
 }
 
 __device__ __forceinline__ uint8_t code_exact(uint16_t h, float mn, float s, float levels) {
@@ -76,11 +97,47 @@ __device__ __forceinline__ uint8_t code_exact(uint16_t h, float mn, float s, flo
   return (uint8_t)fminf(fmaxf(rintf(q), 0.0f), levels);
 }
 
+// One per-token group held in registers: w[4 i + k] holds values 8 p + 2 k
+// and 8 p + 2 k + 1 (low half first) of piece p = (i + rot) & 3 of the
+// group. Codes go to crow[0..31] (LDS, 4-byte aligned), packed four a word;
+// returns scale/zero, y = RN(1 / scale) (0 for a constant group, whose codes
+// are then all 0) and the largest distance of the fast test, for the recode
+// of the values near a rounding boundary that the caller makes.
+__device__ __forceinline__ float code_token32(const uint32_t (&w)[16], int rot, int bits, uint8_t* crow,
+                                              float* scale, float* zero, float* y_out) {
+  float mn, mx;
+  minmax32(w, &mn, &mx);
+  const float levels = (float)((1 << bits) - 1);
+  const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
+  *scale = s;
+  *zero = mn;
+  const float y = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+  *y_out = y;
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      float d0, d1;
+      const uint32_t u = w[4 * i + (k >> 1)];
+      const float r0 = code_half<0>(u, mn, y, &d0), r1 = code_half<1>(u, mn, y, &d1);
+      dmax = fmaxf(dmax, fmaxf(d0, d1));
+      c[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r0, k & 3, c[k >> 2]);
+      c[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r1, (k & 3) + 1, c[k >> 2]);
+    }
+    uint8_t* dst = crow + 8 * ((i + rot) & 3);
+    *(uint32_t*)dst = c[0];
+    *(uint32_t*)(dst + 4) = c[1];
+  }
+  return dmax;
+}
+
 // One per-token group: the 32 fp16 values row[0..31] (LDS, 16-byte aligned)
 // to codes crow[0..31] (LDS, 4-byte aligned); returns scale/zero. The values
 // are read as four 16-byte pieces starting with piece rot & 3 (callers spread
 // the lanes of a wave over the LDS banks with it), held in registers for both
-// passes; the codes are packed four a word before they are stored.
+// passes.
 __device__ __forceinline__ void quantize_token32(const uint16_t* row, int rot, int bits, uint8_t* crow,
                                                  float* scale, float* zero) {
   typedef uint32_t w4_t __attribute__((ext_vector_type(4)));
@@ -90,39 +147,33 @@ __device__ __forceinline__ void quantize_token32(const uint16_t* row, int rot, i
   uint32_t w[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) w[i] = x[i >> 2][i & 3];
-  float mn, mx;
-  minmax32(w, &mn, &mx);
-  const float levels = (float)((1 << bits) - 1);
-  const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
-  *scale = s;
-  *zero = mn;
-  if (s == 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(uint32_t*)(crow + 4 * i) = 0u;
-    return;
-  }
-  const float y = __fdiv_rn(1.0f, s);
-  float dmax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t c[2] = {0u, 0u};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float d;
-      const float r = code_fast((uint16_t)(w[4 * i + (k >> 1)] >> (16 * (k & 1))), mn, y, &d);
-      dmax = fmaxf(dmax, d);
-      c[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r, k & 3, c[k >> 2]);
-    }
-    uint8_t* dst = crow + 8 * ((i + rot) & 3);
-    *(uint32_t*)dst = c[0];
-    *(uint32_t*)(dst + 4) = c[1];
-  }
+  float y;
+  const float dmax = code_token32(w, rot, bits, crow, scale, zero, &y);
   if (dmax > kNear) {  // rare: recode the values near a rounding boundary
+    const float mn = *zero, s = *scale, levels = (float)((1 << bits) - 1);
 #pragma unroll 1
     for (int k = 0; k < GS; ++k) {
       float d;
       (void)code_fast(row[k], mn, y, &d);
       if (d > kNear) crow[k] = code_exact(row[k], mn, s, levels);
+    }
+  }
+}
+
+// The same for a group whose values are in registers in order (rot = 0):
+// the recode reads them with a uniform index.
+__device__ __forceinline__ void quantize_token32_regs(const uint32_t (&w)[16], int bits, uint8_t* crow,
+                                                      float* scale, float* zero) {
+  float y;
+  const float dmax = code_token32(w, 0, bits, crow, scale, zero, &y);
+  if (dmax > kNear) {  // rare: recode the values near a rounding boundary
+    const float mn = *zero, s = *scale, levels = (float)((1 << bits) - 1);
+#pragma unroll 1
+    for (int k = 0; k < GS; ++k) {
+      const uint16_t x = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+      float d;
+      (void)code_fast(x, mn, y, &d);
+      if (d > kNear) crow[k] = code_exact(x, mn, s, levels);
     }
   }
 }
@@ -136,17 +187,14 @@ __device__ __forceinline__ uint32_t lane_xor32(uint32_t x, int h) {
 }
 
 // Two per-channel groups, channels c0 and c0 + 1, by lanes l and l ^ 32 of
-// one wave (h = l >> 5; the whole wave must call): lane h reads the channel
-// pair at rows 2i + h (i < 16) as one 32-bit word (pair: &x[h][c0], row
-// stride D, LDS), the two lanes combine their minima and maxima, lane h
-// computes the scale of channel c0 + h (returned with its zero), and each
-// lane codes its 16 rows of both channels, two codes a 16-bit store (cpair:
-// &codes[h][c0], row stride CS).
-__device__ __forceinline__ void quantize_channel_pair(const uint16_t* pair, int h, int bits, uint8_t* cpair,
-                                                      float* scale, float* zero) {
-  uint32_t w[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) w[i] = *(const uint32_t*)(pair + 2 * i * D);
+// one wave (h = l >> 5; the whole wave must call). w[i] holds the channel
+// pair at row 2i + h (channel c0 in the low half); the two lanes combine
+// their minima and maxima, lane h computes the scale of channel c0 + h
+// (returned with its zero), and each lane codes its 16 rows of both
+// channels, two codes a 16-bit store (cpair: &codes[h][c0], row stride CS).
+// The recode reads the values with a uniform index.
+__device__ __forceinline__ void quantize_channel_pair_regs(const uint32_t (&w)[16], int h, int bits, uint8_t* cpair,
+                                                           float* scale, float* zero) {
   const uint32_t w0 = w[0];
   h2_t lo = __builtin_bit_cast(h2_t, w0), hi = lo;
 #pragma unroll
@@ -177,8 +225,8 @@ __device__ __forceinline__ void quantize_channel_pair(const uint16_t* pair, int 
   for (int i = 0; i < 16; ++i) {
     const uint32_t u = w[i];
     float d0, d1;
-    const float r0 = code_fast((uint16_t)u, mn0, y0, &d0);
-    const float r1 = code_fast((uint16_t)(u >> 16), mn1, y1, &d1);
+    const float r0 = code_half<0>(u, mn0, y0, &d0);
+    const float r1 = code_half<1>(u, mn1, y1, &d1);
     dmax = fmaxf(dmax, fmaxf(d0, d1));
     const uint32_t c = __builtin_amdgcn_cvt_pk_u8_f32(r1, 1, __builtin_amdgcn_cvt_pk_u8_f32(r0, 0, 0u));
     *(uint16_t*)(cpair + 2 * i * CS) = (uint16_t)c;
@@ -188,15 +236,25 @@ __device__ __forceinline__ void quantize_channel_pair(const uint16_t* pair, int 
     const float s0 = h ? sp : s, s1 = h ? s : sp;
 #pragma unroll 1
     for (int i = 0; i < 16; ++i) {
+      const uint32_t u = w[i];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint16_t x = pair[2 * i * D + e];
+        const uint16_t x = (uint16_t)(u >> (16 * e));
         float d;
         (void)code_fast(x, e ? mn1 : mn0, e ? y1 : y0, &d);
         if (d > kNear) cpair[2 * i * CS + e] = code_exact(x, e ? mn1 : mn0, e ? s1 : s0, levels);
       }
     }
   }
+}
+
+// The same with the values read from LDS: pair = &x[h][c0], row stride D.
+__device__ __forceinline__ void quantize_channel_pair(const uint16_t* pair, int h, int bits, uint8_t* cpair,
+                                                      float* scale, float* zero) {
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = *(const uint32_t*)(pair + 2 * i * D);
+  quantize_channel_pair_regs(w, h, bits, cpair, scale, zero);
 }
 
 // Word W = tid + NT k of a code block (NT = 128 or 256 threads, tid < NT):

@@ -124,3 +124,33 @@ def test_token_appends_ties(gpu, oq, fused):
         seq += 1
     torch.cuda.synchronize()
     _check(gpu, oq, plan, cache, ks, vs, L, hkv)
+
+
+def _fp16_range_values(L, seed):
+    """fp16 [L, 128] over the whole finite range: random bit patterns (every exponent, both
+    signs, so denormals, signed zeros and values up to 65504) in the first 64 channels,
+    denormals only in the next 32, and values packed near 1000 in the last 32 (tiny scales
+    beside a large zero point)."""
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 1 << 16, (L, 128), dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7C00) != 0x7C00
+    bits = np.where(finite, bits, bits & 0x83FF)  # exponent 31 -> denormal with the same sign
+    x = bits.view(np.float16).copy()
+    den = (rng.integers(0, 1 << 10, (L, 32)) | (rng.integers(0, 2, (L, 32)) << 15)).astype(np.uint16)
+    x[:, 64:96] = den.view(np.float16)
+    x[:, 96:] = (1000.0 + rng.integers(-40, 40, (L, 32)) * 0.5).astype(np.float16)
+    return x
+
+
+def test_prefill_append_full_fp16_range(gpu, oq):
+    L, hkv = 96, 2
+    plan = gpu.plan_layers(gpu.make_shape(hkv * 2, hkv, 1, max_tokens=L), CFGS)
+    cache = torch.zeros(plan.total_bytes, dtype=torch.uint8, device="cuda")
+    ks = [np.stack([_fp16_range_values(L, 300 + 10 * l + h) for h in range(hkv)]) for l in range(len(CFGS))]
+    vs = [np.stack([_fp16_range_values(L, 400 + 10 * l + h) for h in range(hkv)]) for l in range(len(CFGS))]
+    z = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for l in range(len(CFGS)):
+        gpu.quantize_append(plan, l, cache, torch.from_numpy(ks[l][None]).cuda(), torch.from_numpy(vs[l][None]).cuda(),
+                            z)
+    torch.cuda.synchronize()
+    _check(gpu, oq, plan, cache, ks, vs, L, hkv)
