@@ -149,7 +149,7 @@ class Workload:
         return syn.keys_fp16(self.seed, layer, requests, range(self.Hkv), t0, n, outlier_count=cnt,
                              outlier_factor=fac, num_kv_heads=self.Hkv, device=device)
 
-    def prefill_append_rate(self, reps=3):
+    def prefill_append_rate(self, reps=10):
         """The first layer's prefill for the whole batch in one append call (every full group
         quantized and packed, the rest to the tail), timed with events around `reps` calls. It
         rewrites the same bytes the prefill wrote. Bytes: the fp16 K and V read, the records and
