@@ -59,10 +59,16 @@ __device__ __forceinline__ void minmax32(const uint32_t (&w)[16], float* mn, flo
 // lies within 2^-14 of a half-integer. code_fast returns rint(q) and the
 // distance d of t RN(1 / scale) from it (within 2^-17 of |q - rint(q)|); a
 // value with d > 1/2 - 2^-14 is recoded with the IEEE division (a fraction of
-// a percent of fp16 inputs, exact ties included). No clamp is needed on the
-// fast path: t <= RN(max - min) and y = RN(1 / scale) put q below
+// a percent of fp16 inputs, most of them exact ties). No clamp is needed on
+// the fast path: t <= RN(max - min) and y = RN(1 / scale) put q below
 // levels (1 + 2^-22) < levels + 1/2, and t >= 0.
 constexpr float kNear = 0.5f - 0x1p-14f;
+
+// Bit k of the result is set when value k is near a rounding boundary in some
+// lane of the wave: one compare into a lane mask, the rest scalar.
+__device__ __forceinline__ uint32_t near_bit(float d, int k) {
+  return __builtin_amdgcn_ballot_w64(d > kNear) != 0 ? 1u << k : 0u;
+}
 
 __device__ __forceinline__ float code_of_t(float t, float y, float* d) {
   const float r = rintf(__fmul_rn(t, y));
@@ -97,47 +103,14 @@ __device__ __forceinline__ uint8_t code_exact(uint16_t h, float mn, float s, flo
   return (uint8_t)fminf(fmaxf(rintf(q), 0.0f), levels);
 }
 
-// One per-token group held in registers: w[4 i + k] holds values 8 p + 2 k
-// and 8 p + 2 k + 1 (low half first) of piece p = (i + rot) & 3 of the
-// group. Codes go to crow[0..31] (LDS, 4-byte aligned), packed four a word;
-// returns scale/zero, y = RN(1 / scale) (0 for a constant group, whose codes
-// are then all 0) and the largest distance of the fast test, for the recode
-// of the values near a rounding boundary that the caller makes.
-__device__ __forceinline__ float code_token32(const uint32_t (&w)[16], int rot, int bits, uint8_t* crow,
-                                              float* scale, float* zero, float* y_out) {
-  float mn, mx;
-  minmax32(w, &mn, &mx);
-  const float levels = (float)((1 << bits) - 1);
-  const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
-  *scale = s;
-  *zero = mn;
-  const float y = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
-  *y_out = y;
-  float dmax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t c[2] = {0u, 0u};
-#pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-      float d0, d1;
-      const uint32_t u = w[4 * i + (k >> 1)];
-      const float r0 = code_half<0>(u, mn, y, &d0), r1 = code_half<1>(u, mn, y, &d1);
-      dmax = fmaxf(dmax, fmaxf(d0, d1));
-      c[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r0, k & 3, c[k >> 2]);
-      c[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r1, (k & 3) + 1, c[k >> 2]);
-    }
-    uint8_t* dst = crow + 8 * ((i + rot) & 3);
-    *(uint32_t*)dst = c[0];
-    *(uint32_t*)(dst + 4) = c[1];
-  }
-  return dmax;
-}
-
 // One per-token group: the 32 fp16 values row[0..31] (LDS, 16-byte aligned)
 // to codes crow[0..31] (LDS, 4-byte aligned); returns scale/zero. The values
 // are read as four 16-byte pieces starting with piece rot & 3 (callers spread
-// the lanes of a wave over the LDS banks with it), held in registers for both
-// passes.
+// the lanes of a wave over the LDS banks with it) and held in registers for
+// both passes; codes are packed four a word. Values near a rounding boundary
+// (positions the wave marks together, so the recode loop visits only those)
+// are recoded with the IEEE division; a constant group takes y = 0, so all
+// its codes are 0.
 __device__ __forceinline__ void quantize_token32(const uint16_t* row, int rot, int bits, uint8_t* crow,
                                                  float* scale, float* zero) {
   typedef uint32_t w4_t __attribute__((ext_vector_type(4)));
@@ -147,34 +120,37 @@ __device__ __forceinline__ void quantize_token32(const uint16_t* row, int rot, i
   uint32_t w[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) w[i] = x[i >> 2][i & 3];
-  float y;
-  const float dmax = code_token32(w, rot, bits, crow, scale, zero, &y);
-  if (dmax > kNear) {  // rare: recode the values near a rounding boundary
-    const float mn = *zero, s = *scale, levels = (float)((1 << bits) - 1);
-#pragma unroll 1
-    for (int k = 0; k < GS; ++k) {
-      float d;
-      (void)code_fast(row[k], mn, y, &d);
-      if (d > kNear) crow[k] = code_exact(row[k], mn, s, levels);
+  float mn, mx;
+  minmax32(w, &mn, &mx);
+  const float levels = (float)((1 << bits) - 1);
+  const float s = __fdiv_rn(__fsub_rn(mx, mn), levels);
+  *scale = s;
+  *zero = mn;
+  const float y = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
+  uint32_t near = 0;  // bit 8 i + k: value k of the piece read i-th
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      float d0, d1;
+      const uint32_t u = w[4 * i + (k >> 1)];
+      const float r0 = code_half<0>(u, mn, y, &d0), r1 = code_half<1>(u, mn, y, &d1);
+      near |= near_bit(d0, 8 * i + k) | near_bit(d1, 8 * i + k + 1);
+      c[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r0, k & 3, c[k >> 2]);
+      c[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(r1, (k & 3) + 1, c[k >> 2]);
     }
+    uint8_t* dst = crow + 8 * ((i + rot) & 3);
+    *(uint32_t*)dst = c[0];
+    *(uint32_t*)(dst + 4) = c[1];
   }
-}
-
-// The same for a group whose values are in registers in order (rot = 0):
-// the recode reads them with a uniform index.
-__device__ __forceinline__ void quantize_token32_regs(const uint32_t (&w)[16], int bits, uint8_t* crow,
-                                                      float* scale, float* zero) {
-  float y;
-  const float dmax = code_token32(w, 0, bits, crow, scale, zero, &y);
-  if (dmax > kNear) {  // rare: recode the values near a rounding boundary
-    const float mn = *zero, s = *scale, levels = (float)((1 << bits) - 1);
-#pragma unroll 1
-    for (int k = 0; k < GS; ++k) {
-      const uint16_t x = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
-      float d;
-      (void)code_fast(x, mn, y, &d);
-      if (d > kNear) crow[k] = code_exact(x, mn, s, levels);
-    }
+  while (near != 0) {  // rare
+    const int b = __builtin_ctz(near);
+    near &= near - 1;
+    const int pos = 8 * (((b >> 3) + rot) & 3) + (b & 7);
+    float d;
+    (void)code_fast(row[pos], mn, y, &d);
+    if (d > kNear) crow[pos] = code_exact(row[pos], mn, s, levels);
   }
 }
 
@@ -187,14 +163,18 @@ __device__ __forceinline__ uint32_t lane_xor32(uint32_t x, int h) {
 }
 
 // Two per-channel groups, channels c0 and c0 + 1, by lanes l and l ^ 32 of
-// one wave (h = l >> 5; the whole wave must call). w[i] holds the channel
-// pair at row 2i + h (channel c0 in the low half); the two lanes combine
-// their minima and maxima, lane h computes the scale of channel c0 + h
-// (returned with its zero), and each lane codes its 16 rows of both
-// channels, two codes a 16-bit store (cpair: &codes[h][c0], row stride CS).
-// The recode reads the values with a uniform index.
-__device__ __forceinline__ void quantize_channel_pair_regs(const uint32_t (&w)[16], int h, int bits, uint8_t* cpair,
-                                                           float* scale, float* zero) {
+// one wave (h = l >> 5; the whole wave must call): lane h reads the channel
+// pair at rows 2i + h (i < 16) as one 32-bit word (pair: &x[h][c0], row
+// stride D, LDS), the two lanes combine their minima and maxima, lane h
+// computes the scale of channel c0 + h (returned with its zero), and each
+// lane codes its 16 rows of both channels, two codes a 16-bit store (cpair:
+// &codes[h][c0], row stride CS). Values near a rounding boundary are recoded
+// as in quantize_token32.
+__device__ __forceinline__ void quantize_channel_pair(const uint16_t* pair, int h, int bits, uint8_t* cpair,
+                                                      float* scale, float* zero) {
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = *(const uint32_t*)(pair + 2 * i * D);
   const uint32_t w0 = w[0];
   h2_t lo = __builtin_bit_cast(h2_t, w0), hi = lo;
 #pragma unroll
@@ -220,41 +200,28 @@ __device__ __forceinline__ void quantize_channel_pair_regs(const uint32_t (&w)[1
   const float y = s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s);
   const float yp = __builtin_bit_cast(float, lane_xor32(__builtin_bit_cast(uint32_t, y), h));
   const float y0 = h ? yp : y, y1 = h ? y : yp;
-  float dmax = 0.0f;
+  uint32_t near = 0;  // bit 2 i + e: row 2i + h, channel c0 + e
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t u = w[i];
     float d0, d1;
     const float r0 = code_half<0>(u, mn0, y0, &d0);
     const float r1 = code_half<1>(u, mn1, y1, &d1);
-    dmax = fmaxf(dmax, fmaxf(d0, d1));
+    near |= near_bit(d0, 2 * i) | near_bit(d1, 2 * i + 1);
     const uint32_t c = __builtin_amdgcn_cvt_pk_u8_f32(r1, 1, __builtin_amdgcn_cvt_pk_u8_f32(r0, 0, 0u));
     *(uint16_t*)(cpair + 2 * i * CS) = (uint16_t)c;
   }
   const float sp = __builtin_bit_cast(float, lane_xor32(__builtin_bit_cast(uint32_t, s), h));
-  if (dmax > kNear) {  // rare: recode the values near a rounding boundary
-    const float s0 = h ? sp : s, s1 = h ? s : sp;
-#pragma unroll 1
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t u = w[i];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint16_t x = (uint16_t)(u >> (16 * e));
-        float d;
-        (void)code_fast(x, e ? mn1 : mn0, e ? y1 : y0, &d);
-        if (d > kNear) cpair[2 * i * CS + e] = code_exact(x, e ? mn1 : mn0, e ? s1 : s0, levels);
-      }
-    }
+  const float s0 = h ? sp : s, s1 = h ? s : sp;
+  while (near != 0) {  // rare
+    const int b = __builtin_ctz(near);
+    near &= near - 1;
+    const int i = b >> 1, e = b & 1;
+    const uint16_t x = pair[2 * i * D + e];
+    float d;
+    (void)code_fast(x, e ? mn1 : mn0, e ? y1 : y0, &d);
+    if (d > kNear) cpair[2 * i * CS + e] = code_exact(x, e ? mn1 : mn0, e ? s1 : s0, levels);
   }
-}
-
-// The same with the values read from LDS: pair = &x[h][c0], row stride D.
-__device__ __forceinline__ void quantize_channel_pair(const uint16_t* pair, int h, int bits, uint8_t* cpair,
-                                                      float* scale, float* zero) {
-  uint32_t w[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) w[i] = *(const uint32_t*)(pair + 2 * i * D);
-  quantize_channel_pair_regs(w, h, bits, cpair, scale, zero);
 }
 
 // Word W = tid + NT k of a code block (NT = 128 or 256 threads, tid < NT):
