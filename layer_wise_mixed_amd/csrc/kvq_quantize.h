@@ -5,7 +5,10 @@
 // group size 32): scale = (max - min) / (2^b - 1) in fp32, zero = min,
 // code = clamp(rint((x - zero) / scale), 0, 2^b - 1) with IEEE subtraction
 // and division (explicitly rounded operations, so no contraction can change
-// them) and round-half-even; a constant group gets scale 0 and codes 0.
+// them) and round-half-even; a constant group gets scale 0 and codes 0. The
+// codes come from a reciprocal quotient, with the IEEE division only for the
+// values whose quotient lies near a rounding boundary (code_fast): the same
+// codes, bit for bit.
 #pragma once
 
 #include "kvq_internal.h"

@@ -186,7 +186,7 @@ struct Lane {
 };
 
 struct Acc {
-  f4_t o[8], ol[8];  // P.V with the high and with the (2^11-scaled) low parts of Pt
+  f4_t o[8], ol[8];  // P.V with the high and with the (2^10-scaled) low parts of Pt
   float m, lpart, zpart[4];
 };
 
