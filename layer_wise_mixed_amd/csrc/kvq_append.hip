@@ -235,21 +235,30 @@ hipError_t launch_dequant_paged(const DequantArgs& a, int batch, hipStream_t s) 
   return hipGetLastError();
 }
 
-// (run, stream) workgroups per tensor of a long append: with both tensors
-// about 2.5 rounds of the 8 two-wave workgroups a CU holds at this kernel's
-// register count (256 CUs); measured faster than 1,920 or 3,840
-constexpr int kAppendRuns = 2560;
+// (run, stream) workgroups per tensor of a long append, about: with both
+// tensors about 4.5 rounds of the 8 two-wave workgroups a CU holds at this
+// kernel's register count (256 CUs). Measured on a 2047-token prefill of 512
+// streams (63 full groups each): runs of 13 groups (2,560 workgroups a
+// tensor) 163-165 us, of 9 (3,584) 159-163 us, of 7 (4,608) 157-160 us, of 8
+// (4,096) 204-207 us. A run of 2^k groups starts 2^k x 8 KiB into its
+// stream's fp16 input, and that stride is avoided.
+constexpr int kAppendRuns = 4608;
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t s, const EventPair* ev) {
   const int y = a.n_new > 0 ? (a.n_new + GS - 1) / GS : 0;
   if (y == 0 || batch == 0) return hipSuccess;
   // long appends (prefill): about kAppendRuns (run, stream) workgroups per
-  // tensor, each looping over a run of its stream's groups; short ones: a
+  // tensor, each looping over a run of equal length of its stream's groups
+  // (sized on the full groups of an append to an empty stream); short ones: a
   // workgroup per group
   const int streams = batch * a.geo.hkv;
   int x = y;
   if (y > 8) {
-    x = (kAppendRuns + streams - 1) / streams;
+    const int full = a.n_new / GS;
+    const int x0 = (kAppendRuns + streams - 1) / streams;
+    int r = (full + x0 - 1) / x0;  // groups a run
+    if (r >= 4 && (r & (r - 1)) == 0) --r;
+    x = (full + r - 1) / r;
     if (x > y) x = y;
   }
   return launch_timed(append_kernel, dim3(x, streams, 2), dim3(128), s, ev, a);
