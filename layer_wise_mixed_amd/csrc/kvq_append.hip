@@ -38,13 +38,14 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   const uint16_t* src = (is_v ? a.v_new : a.k_new) + (size_t)sigma * a.n_new * D;
 
   // a whole-new group's 32 contiguous rows of this tensor, 8 KiB: four
-  // 16-byte pieces a thread
+  // 16-byte pieces a thread, non-temporal (read once; measured 4-15% faster
+  // for the whole prompt than ordinary loads)
   constexpr int kPer = GS * D / 8 / 128;
   u4_t xa[kPer];
   auto fetch = [&](int y) {
     const u4_t* xsrc = (const u4_t*)(src + (size_t)(GS * (m0 + y) - L0) * D);
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) xa[q] = xsrc[tid + 128 * q];
+    for (int q = 0; q < kPer; ++q) xa[q] = __builtin_nontemporal_load(&xsrc[tid + 128 * q]);
   };
   auto whole_new = [&](int y) { return GS * (m0 + y) >= L0; };
 
